@@ -1,0 +1,155 @@
+/*
+ * saq.h - C ABI of the joint-sequence QKNorm + 3D RoPE -> block selection ->
+ * block-sparse attention layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the per-layer self-attention of a video+audio diffusion
+ * transformer over one joint token sequence (Sol Engine "H3 on device" page:
+ * intro, which says this attention dominates the profile; lossless-kernels
+ * fusion table, row "fused QKNorm + RoPE"; Sol-Attn paragraph, which computes
+ * only the attention blocks a per-step selection keeps).
+ *
+ * Conventions shared by every call:
+ *  - Tensors q, k, v, o are bf16, shape [B, S, H, D], contiguous (D fastest),
+ *    in device memory owned by the caller, 16-byte aligned.
+ *  - Block masks are uint8 [B, H, nB, nB] with nB = ceil(S / block); block i
+ *    holds tokens [i*block, min((i+1)*block, S)), so the last block may be
+ *    partial.
+ *  - Supported: D in {64, 128}; block in {64, 128}; 1 <= S; nB <= 4096;
+ *    1 <= B, H; B*S*H*D < 2^31.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls are asynchronous on that stream; the library allocates nothing,
+ *    keeps no state between calls and is safe to call from several threads.
+ *  - Every argument is validated on the host before any launch; a call that
+ *    returns non-zero has launched nothing. Device-side faults surface at the
+ *    caller's next synchronisation, as for any HIP launch.
+ *  - Return value: SAQ_OK (0) or a negative SAQ_ERR_* code; nothing crosses
+ *    the ABI as an exception. saq_status_string() names the code and
+ *    saq_last_hip_error() returns the HIP error of the calling thread's last
+ *    SAQ_ERR_HIP.
+ */
+#ifndef SAQ_H
+#define SAQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum saq_status {
+    SAQ_OK = 0,
+    SAQ_ERR_NULL = -1,         /* a required pointer is NULL */
+    SAQ_ERR_SHAPE = -2,        /* a size is <= 0, inconsistent, or too large */
+    SAQ_ERR_UNSUPPORTED = -3,  /* D or block outside the supported set */
+    SAQ_ERR_ALIGN = -4,        /* a tensor pointer is not 16-byte aligned */
+    SAQ_ERR_RANGE = -5,        /* keep_ratio, eps, base or scale out of range */
+    SAQ_ERR_WORKSPACE = -6,    /* workspace too small or NULL */
+    SAQ_ERR_HIP = -7,          /* a HIP call failed; see saq_last_hip_error() */
+    SAQ_ERR_NO_DEVICE = -8,    /* no HIP device is visible */
+    SAQ_ERR_ALIAS = -9         /* an output overlaps an input it must not */
+};
+
+/*
+ * Fused QKNorm + 3D multimodal RoPE, in place on q and k.
+ * (Sol Engine "H3 on device" page, fusion table, row "fused QKNorm + RoPE":
+ * the fused kernel replaces two read/write passes over Q and K.)
+ *
+ * For every (b, s, h) row x of q (weight w_q) and of k (weight w_k):
+ *   x_hat[d] = x[d] / sqrt(mean_d(x^2) + eps) * w[d]
+ * then head_dim is split into contiguous sections of widths (dt, dh, dw) for
+ * the axes (t, h, w); in the section of axis a, each adjacent pair
+ * (2i, 2i+1) is rotated by theta = pos_thw[s][a] * rope_base^(-2i/d_a):
+ *   (x0, x1) <- (x0 cos theta - x1 sin theta, x0 sin theta + x1 cos theta).
+ * The norm and rotation run in fp32 (angles in fp64), the result is rounded
+ * to bf16 (nearest-even) and written back in place.
+ *
+ *   q, k     bf16 [B,S,H,D], read and overwritten.
+ *   pos_thw  int32 [S,3] device array of (t, h, w) positions, shared by all
+ *            batch entries; any values are allowed.
+ *   w_q, w_k fp32 [D] device arrays.
+ *   dt+dh+dw must equal D, each even and >= 0 (multiples of 8 for speed are
+ *   not required). rope_base > 1, eps > 0, both finite.
+ * q and k must not overlap.
+ */
+int saq_qknorm_rope(void* q, void* k, const int32_t* pos_thw, const float* w_q, const float* w_k,
+                    int32_t B, int32_t S, int32_t H, int32_t D, int32_t dt, int32_t dh, int32_t dw,
+                    double rope_base, double eps, void* stream);
+
+/*
+ * Out-of-place form of saq_qknorm_rope: reads q_in, k_in and writes q_out,
+ * k_out (same shapes). Each output may equal its own input (then it is the
+ * in-place call) but must not partially overlap any other tensor.
+ */
+int saq_qknorm_rope_out(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                        const int32_t* pos_thw, const float* w_q, const float* w_k,
+                        int32_t B, int32_t S, int32_t H, int32_t D, int32_t dt, int32_t dh, int32_t dw,
+                        double rope_base, double eps, void* stream);
+
+/*
+ * Number of key blocks kept per query block:
+ *   k = clamp(ceil(keep_ratio * nB - 1e-6), 1, nB),
+ * evaluated in fp64 (the 1e-6 guard keeps rounding error from raising k).
+ * Returns SAQ_ERR_RANGE for keep_ratio outside (0, 1] or NaN, SAQ_ERR_SHAPE
+ * for nB < 1. Pure host function.
+ */
+int32_t saq_kept_blocks(double keep_ratio, int32_t nB);
+
+/* Bytes of device workspace saq_select_blocks needs for these sizes, or 0 if
+ * the sizes are invalid. Pure host function. */
+size_t saq_select_blocks_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block);
+
+/*
+ * Training-free dynamic block selection (Sol-Attn paragraph of the Sol Engine
+ * "H3 on device" page: only the (query block, key block) tiles the selection
+ * keeps are computed; KOCPC article on Sol-H3, "Specific outcomes": the
+ * selection is made dynamically at inference time). The pages do not give the
+ * rule; this call implements the following one, per (b, h):
+ *   1. p_i = mean of the rows of block i (fp64; exact sums of bf16 values),
+ *      for q and k separately;
+ *   2. s_ij = sum_d pq_i[d] * pk_j[d] in fp64, d ascending, each product and
+ *      each sum rounded separately (no fused multiply-add);
+ *   3. row i keeps block i plus the k-1 largest s_ij over j != i, with
+ *      k = saq_kept_blocks(keep_ratio, nB); ties go to the lower j and -0.0
+ *      equals +0.0.
+ * Output: block_mask [B,H,nB,nB] uint8 with exactly k ones per row and a one
+ * on the diagonal. Bit-for-bit deterministic. Inputs must be finite.
+ *
+ *   q, k       bf16 [B,S,H,D]: the post-prologue tensors attention consumes.
+ *   workspace  device buffer of at least
+ *              saq_select_blocks_workspace_bytes(B,S,H,D,block) bytes,
+ *              256-byte aligned; its contents are scratch.
+ */
+int saq_select_blocks(const void* q, const void* k, int32_t B, int32_t S, int32_t H, int32_t D,
+                      int32_t block, double keep_ratio, uint8_t* block_mask, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse flash attention (Sol-Attn paragraph of the Sol Engine "H3 on
+ * device" page: attention computed only on the kept blocks, with an online
+ * softmax). For each (b, h, query block i), over the kept key blocks j in
+ * ascending order:
+ *   o_t = sum_{u in kept tokens} softmax_u(q_t . k_u * scale) v_u,
+ * non-causal, every valid token of a kept block taking part. QK^T and PV run
+ * on bf16 MFMA with fp32 accumulation; softmax statistics are fp32; the
+ * result is rounded to bf16. A query block with no kept key block gets
+ * o = 0. Any 0/1 mask is accepted (a non-zero byte counts as 1).
+ *
+ *   softmax_scale  > 0, or <= 0 to mean 1/sqrt(D); must be finite.
+ *   o              bf16 [B,S,H,D]; must not overlap q, k, v or block_mask.
+ */
+int saq_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* block_mask,
+                          int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
+                          float softmax_scale, void* o, void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* saq_status_string(int status);
+
+/* The hipError_t of the calling thread's most recent SAQ_ERR_HIP (0 if none). */
+int saq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAQ_H */

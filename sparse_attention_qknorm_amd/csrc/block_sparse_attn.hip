@@ -1,0 +1,272 @@
+// Block-sparse flash attention for gfx950 (bf16 MFMA, fp32 online softmax).
+//
+// Sol-Attn paragraph of the Sol Engine "H3 on device" page: attention over the
+// joint video+audio sequence computes only the (query block, key block) tiles
+// that the selection keeps, inside an online-softmax pass.
+//
+// One workgroup per (b, h, query block i); BLOCK/32 wavefronts, each owning 32
+// query rows. For every kept key block j (ascending):
+//   S^T = K_j Q_i^T    v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q^T held in
+//                      registers for the whole loop;
+//   online softmax     each lane holds one query row (lane % 32) and half of the
+//                      keys of every 32-key tile, so row maxima and sums are
+//                      lane-local plus one exchange with lane ^ 32;
+//   O^T += V_j^T P^T   A = V^T from LDS, B = P^T re-packed from the S^T
+//                      accumulators without any data movement: the key order
+//                      inside a 16-key MFMA step is permuted to match the
+//                      accumulator layout, and V is staged in LDS with four
+//                      consecutive keys interleaved per d ([key/4][d][4]) so
+//                      each lane reads its keys with 8-byte loads.
+// O^T accumulates with each lane holding its own query row, so the rescale by
+// exp2(m_old - m_new) and the final 1/l are lane-local. Keys past S score -inf
+// (and K/V rows past S are staged as zeros); rows past S are not stored.
+// Workgroups are renumbered so every XCD (own L2) works through adjacent query
+// blocks of the same head, whose kept key blocks overlap.
+#include "common.h"
+#include "kernels.h"
+
+namespace saq {
+
+namespace {
+
+template <int BLOCK, int D>
+struct AttnShape {
+    static constexpr int kWaves = BLOCK / 32;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int kKeyTiles = BLOCK / 32;        // 32-key tiles of S^T
+    static constexpr int kDSteps = D / 16;              // k-steps of the QK^T product
+    static constexpr int kDTiles = D / 32;              // 32-wide d tiles of O^T
+    static constexpr int kKeySteps = BLOCK / 16;        // k-steps of the PV product
+    static constexpr int kKPitch = D + 8;               // bf16 elements per staged K row (16 B pad)
+    static constexpr int kVPitch = D * 4;               // bf16 elements per staged group of 4 keys
+    static constexpr int kKChunks = BLOCK * D / 8;      // 16-byte chunks of a K tile
+    static constexpr int kVUnits = (BLOCK / 4) * (D / 2);  // (4 keys x 2 d) units of a V tile
+    static constexpr int kKPerThread = kKChunks / kThreads;
+    static constexpr int kVPerThread = kVUnits / kThreads;
+    static_assert(kThreads == BLOCK * 2, "launch bound of the kernel");
+    static_assert(kKChunks % kThreads == 0 && kVUnits % kThreads == 0, "tile split");
+};
+
+template <int BLOCK, int D>
+__global__ __launch_bounds__(BLOCK * 2) void block_sparse_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint8_t* __restrict__ mask, uint16_t* __restrict__ o, int32_t S, int32_t H, int32_t nB,
+    int64_t n_items, float scale_log2) {
+    using Sh = AttnShape<BLOCK, D>;
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BLOCK * Sh::kKPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[(BLOCK / 4) * Sh::kVPitch];
+    __shared__ uint16_t kept[kMaxBlocks];
+    __shared__ int n_kept_s;
+
+    const int64_t item = xcd_contiguous_index(blockIdx.x, n_items);
+    const int i = (int)(item % nB);
+    const int64_t bh = item / nB;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int l32 = lane % 32;
+    const int g = lane / 32;
+
+    // ---- compact the mask row into an ascending list of kept key blocks (wave 0)
+    if (wave == 0) {
+        const uint8_t* mrow = mask + item * (int64_t)nB;
+        int count = 0;
+        for (int j0 = 0; j0 < nB; j0 += kWave) {
+            const int j = j0 + lane;
+            const bool keep = j < nB && mrow[j] != 0;
+            const uint64_t bits = __ballot(keep);
+            if (keep) kept[count + __popcll(bits & ((1ull << lane) - 1ull))] = (uint16_t)j;
+            count += __popcll(bits);
+        }
+        if (lane == 0) n_kept_s = count;
+    }
+
+    const int64_t row_stride = (int64_t)H * D;          // elements between consecutive tokens
+    const int64_t head_off = b * (int64_t)S * row_stride + (int64_t)h * D;
+
+    // ---- Q^T as the B operand: lane holds query row (32*wave + l32), d = 16*step + 8*g + [0..7]
+    bf16x8 qb[Sh::kDSteps];
+    {
+        const int qrow = i * BLOCK + wave * 32 + l32;
+        if (qrow < S) {
+            const uint16_t* src = q + head_off + (int64_t)qrow * row_stride + 8 * g;
+#pragma unroll
+            for (int st = 0; st < Sh::kDSteps; ++st) qb[st] = *(const bf16x8*)(src + 16 * st);
+        } else {
+#pragma unroll
+            for (int st = 0; st < Sh::kDSteps; ++st) qb[st] = (bf16x8){};
+        }
+    }
+
+    f32x16 oacc[Sh::kDTiles];
+#pragma unroll
+    for (int t = 0; t < Sh::kDTiles; ++t) oacc[t] = (f32x16){};
+    float m_run = -INFINITY;   // running max of the scaled (log2-domain) scores of this lane's row
+    float l_run = 0.f;         // this lane's share of the row's softmax denominator
+
+    __syncthreads();
+    const int n_kept = n_kept_s;
+
+    uint4 kreg[Sh::kKPerThread];
+    uint32_t vreg[Sh::kVPerThread][4];
+
+    auto load_tile = [&](int j) {
+        const int key0 = j * BLOCK;
+#pragma unroll
+        for (int n = 0; n < Sh::kKPerThread; ++n) {
+            const int c = tid + n * Sh::kThreads;
+            const int r = c / (D / 8);
+            const int ch = c % (D / 8);
+            const int key = key0 + r;
+            kreg[n] = key < S ? *(const uint4*)(k + head_off + (int64_t)key * row_stride + 8 * ch)
+                              : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int n = 0; n < Sh::kVPerThread; ++n) {
+            const int u = tid + n * Sh::kThreads;
+            const int dp = u % (D / 2);
+            const int g4 = u / (D / 2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 4 * g4 + r;
+                vreg[n][r] = key < S ? *(const uint32_t*)(v + head_off + (int64_t)key * row_stride + 2 * dp) : 0u;
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int n = 0; n < Sh::kKPerThread; ++n) {
+            const int c = tid + n * Sh::kThreads;
+            const int r = c / (D / 8);
+            const int ch = c % (D / 8);
+            *(uint4*)(k_lds + r * Sh::kKPitch + 8 * ch) = kreg[n];
+        }
+#pragma unroll
+        for (int n = 0; n < Sh::kVPerThread; ++n) {
+            const int u = tid + n * Sh::kThreads;
+            const int dp = u % (D / 2);
+            const int g4 = u / (D / 2);
+            const uint32_t* w = vreg[n];
+            uint4 packed;
+            packed.x = (w[0] & 0xffffu) | (w[1] << 16);            // d = 2dp, keys 0,1
+            packed.y = (w[2] & 0xffffu) | (w[3] << 16);            // d = 2dp, keys 2,3
+            packed.z = (w[0] >> 16) | (w[1] & 0xffff0000u);        // d = 2dp+1, keys 0,1
+            packed.w = (w[2] >> 16) | (w[3] & 0xffff0000u);        // d = 2dp+1, keys 2,3
+            *(uint4*)(v_lds + g4 * Sh::kVPitch + (2 * dp) * 4) = packed;
+        }
+    };
+
+    if (n_kept > 0) load_tile(kept[0]);
+
+    for (int n = 0; n < n_kept; ++n) {
+        const int j = kept[n];
+        __syncthreads();                       // previous tile fully consumed
+        store_tile();
+        __syncthreads();
+        if (n + 1 < n_kept) load_tile(kept[n + 1]);   // next tile's global loads overlap this tile's math
+
+        // ---- S^T tile: rows = keys, cols = this wave's 32 query rows
+        f32x16 sacc[Sh::kKeyTiles];
+#pragma unroll
+        for (int kt = 0; kt < Sh::kKeyTiles; ++kt) {
+            sacc[kt] = (f32x16){};
+            const uint16_t* krow = k_lds + (kt * 32 + l32) * Sh::kKPitch + 8 * g;
+#pragma unroll
+            for (int st = 0; st < Sh::kDSteps; ++st) {
+                const bf16x8 a = *(const bf16x8*)(krow + 16 * st);
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[st], sacc[kt], 0, 0, 0);
+            }
+        }
+
+        // ---- online softmax (log2 domain); acc v of tile kt holds key 32kt + 8(v/4) + 4g + v%4
+        const int key0 = j * BLOCK;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < Sh::kKeyTiles; ++kt)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const int key = key0 + kt * 32 + 8 * (vv / 4) + 4 * g + (vv % 4);
+                const float sv = key < S ? sacc[kt][vv] * scale_log2 : -INFINITY;
+                sacc[kt][vv] = sv;
+                mx = fmaxf(mx, sv);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);              // finite: every kept block has a valid key
+        const float alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.f;
+        bf16x8 pb[Sh::kKeySteps];
+#pragma unroll
+        for (int ks = 0; ks < Sh::kKeySteps; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = exp2f(sacc[ks / 2][8 * (ks % 2) + e] - m_new);
+                psum += p;
+                pb[ks][e] = (__bf16)p;
+            }
+        }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int t = 0; t < Sh::kDTiles; ++t) oacc[t] *= alpha;
+
+        // ---- O^T += V^T P^T; k-index 8g + e of step ks is key 16ks + 8(e/4) + 4g + e%4
+#pragma unroll
+        for (int t = 0; t < Sh::kDTiles; ++t) {
+            const int d = t * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < Sh::kKeySteps; ++ks) {
+                const uint16_t* vp = v_lds + (4 * ks + g) * Sh::kVPitch + d * 4;
+                const bf16x4 lo = *(const bf16x4*)vp;
+                const bf16x4 hi = *(const bf16x4*)(vp + 2 * Sh::kVPitch);
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], oacc[t], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- normalise and store: lane holds row l32 and d = 32t + 8(v/4) + 4g + v%4
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const int qrow = i * BLOCK + wave * 32 + l32;
+    if (qrow < S) {
+        uint16_t* dst = o + head_off + (int64_t)qrow * row_stride;
+#pragma unroll
+        for (int t = 0; t < Sh::kDTiles; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                uint2 w;
+                w.x = f32_to_bf16_bits(oacc[t][4 * m + 0] * inv) | (f32_to_bf16_bits(oacc[t][4 * m + 1] * inv) << 16);
+                w.y = f32_to_bf16_bits(oacc[t][4 * m + 2] * inv) | (f32_to_bf16_bits(oacc[t][4 * m + 3] * inv) << 16);
+                *(uint2*)(dst + t * 32 + 8 * m + 4 * g) = w;
+            }
+    }
+}
+
+template <int BLOCK, int D>
+hipError_t launch_impl(const void* q, const void* k, const void* v, const uint8_t* mask, int32_t B, int32_t S,
+                       int32_t H, float scale, void* o, hipStream_t stream) {
+    using Sh = AttnShape<BLOCK, D>;
+    const int32_t nB = (S + BLOCK - 1) / BLOCK;
+    const int64_t n_items = (int64_t)B * H * nB;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL((block_sparse_attn_kernel<BLOCK, D>), dim3((unsigned)n_items), dim3(Sh::kThreads), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, mask, (uint16_t*)o, S, H, nB,
+                       n_items, scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* mask,
+                                    int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
+                                    float scale, void* o, hipStream_t stream) {
+    if (block == 128 && D == 128) return launch_impl<128, 128>(q, k, v, mask, B, S, H, scale, o, stream);
+    if (block == 128 && D == 64) return launch_impl<128, 64>(q, k, v, mask, B, S, H, scale, o, stream);
+    if (block == 64 && D == 128) return launch_impl<64, 128>(q, k, v, mask, B, S, H, scale, o, stream);
+    return launch_impl<64, 64>(q, k, v, mask, B, S, H, scale, o, stream);
+}
+
+}  // namespace saq

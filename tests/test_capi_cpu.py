@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments with the documented status codes before
+any HIP call (no compute runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from sparse_attention_qknorm_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "saq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_binding.LIB_PATH),
+                                reason="libsaq.so not built (python -m sparse_attention_qknorm_amd.build)")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|const char\*)\s+(saq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared()
+    for n in ("saq_qknorm_rope", "saq_select_blocks", "saq_block_sparse_attn", "saq_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(_binding.LIB_PATH)
+    for name in _declared():
+        assert hasattr(handle, name), name
+    assert sorted(n for n, _, _ in _binding.SIGNATURES) == _declared()
+
+
+def test_status_strings():
+    lib = _binding.lib()
+    for code in range(0, -10, -1):
+        s = lib.saq_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.saq_status_string(-99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("keep,nB", [(0.5, 16), (0.25, 64), (0.2, 256), (0.15, 993), (0.1, 993), (0.3, 993),
+                                     (0.3, 10), (1e-9, 5), (1.0, 1), (1.0, 4096), (0.7, 10), (0.999999, 7)])
+def test_kept_blocks_matches_oracle_rule(keep, nB):
+    assert _binding.lib().saq_kept_blocks(keep, nB) == oracle.num_kept_blocks(keep, nB)
+
+
+def test_kept_blocks_errors():
+    lib = _binding.lib()
+    assert lib.saq_kept_blocks(0.0, 10) == -5
+    assert lib.saq_kept_blocks(1.01, 10) == -5
+    assert lib.saq_kept_blocks(float("nan"), 10) == -5
+    assert lib.saq_kept_blocks(0.5, 0) == -2
+
+
+def test_workspace_bytes():
+    lib = _binding.lib()
+    nB = 993
+    pooled = 2 * 40 * nB * 128 * 8
+    want = (pooled + 255) // 256 * 256 + 40 * nB * nB * 8
+    assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 128, 128) == want
+    assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 96, 128) == 0     # unsupported D
+    assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 128, 32) == 0     # unsupported block
+    assert lib.saq_select_blocks_workspace_bytes(1, 0, 40, 128, 128) == 0
+    assert lib.saq_select_blocks_workspace_bytes(1, 64 * 4097, 1, 64, 64) == 0    # nB > 4096
+
+
+FAKE = 0x10000          # a 16-byte aligned address that is never dereferenced: every call below
+MISALIGNED = 0x10008    # fails validation on the host before any HIP call
+
+
+def test_qknorm_rope_validation():
+    lib = _binding.lib()
+    args = dict(q=FAKE, k=FAKE * 2, pos=FAKE * 3, wq=FAKE * 4, wk=FAKE * 5)
+
+    def call(q=args["q"], k=args["k"], pos=args["pos"], wq=args["wq"], wk=args["wk"], B=1, S=16, H=2, D=64,
+             dt=16, dh=24, dw=24, base=1e4, eps=1e-6):
+        return lib.saq_qknorm_rope(q, k, pos, wq, wk, B, S, H, D, dt, dh, dw, base, eps, None)
+
+    assert call(q=None) == -1 and call(pos=None) == -1 and call(wk=None) == -1
+    assert call(S=0) == -2 and call(H=-1) == -2
+    assert call(D=96, dt=32, dh=32, dw=32) == -3
+    assert call(dt=16, dh=24, dw=22) == -2            # sections do not sum to D
+    assert call(dt=15, dh=25, dw=24) == -2            # odd section
+    assert call(base=1.0) == -5 and call(eps=0.0) == -5 and call(eps=float("inf")) == -5
+    assert call(q=MISALIGNED) == -4
+    assert call(k=FAKE + 16) == -9                    # q and k overlap
+    assert call(B=4096, S=4096, H=4, D=64) == -2      # > 2^31 elements
+
+
+def test_qknorm_rope_out_aliasing():
+    lib = _binding.lib()
+    base = 1 << 20
+    n = 16 * 2 * 64 * 2
+    # q_out overlapping k_in is rejected; q_out == q_in (in place) passes validation
+    st = lib.saq_qknorm_rope_out(base, base + 4 * n, base + 4 * n, base + 8 * n, FAKE, FAKE, FAKE,
+                                 1, 16, 2, 64, 16, 24, 24, 1e4, 1e-6, None)
+    assert st == -9
+    st = lib.saq_qknorm_rope_out(base, base + 4 * n, base + 16, base + 8 * n, FAKE, FAKE, FAKE,
+                                 1, 16, 2, 64, 16, 24, 24, 1e4, 1e-6, None)
+    assert st == -9                                    # partial overlap of q_out with q_in
+
+
+def test_select_blocks_validation():
+    lib = _binding.lib()
+    ws = 1 << 24
+
+    def call(q=FAKE, k=FAKE * 2, B=1, S=1024, H=2, D=64, block=64, keep=0.5, mask=FAKE * 3, w=ws,
+             wbytes=1 << 22):
+        return lib.saq_select_blocks(q, k, B, S, H, D, block, keep, mask, w, wbytes, None)
+
+    assert call(q=None) == -1 and call(mask=None) == -1
+    assert call(block=32) == -3 and call(D=32) == -3
+    assert call(keep=0.0) == -5 and call(keep=1.5) == -5
+    assert call(w=None) == -6 and call(wbytes=16) == -6
+    assert call(w=ws + 16) == -4                       # workspace must be 256-byte aligned
+    assert call(q=MISALIGNED) == -4
+
+
+def test_block_sparse_attn_validation():
+    lib = _binding.lib()
+
+    def call(q=FAKE, k=FAKE * 2, v=FAKE * 3, mask=FAKE * 4, B=1, S=1024, H=2, D=64, block=64, scale=0.0,
+             o=1 << 24):
+        return lib.saq_block_sparse_attn(q, k, v, mask, B, S, H, D, block, scale, o, None)
+
+    assert call(o=None) == -1 and call(v=None) == -1
+    assert call(block=256) == -3
+    assert call(scale=float("nan")) == -5
+    assert call(o=FAKE * 3) == -9                      # o aliases v
+    assert call(o=(1 << 24) + 8) == -4
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="only meaningful on a host without a GPU")
+def test_valid_call_without_device_reports_no_device():
+    lib = _binding.lib()
+    st = lib.saq_block_sparse_attn(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, 1024, 2, 64, 64, 0.0, 1 << 24, None)
+    assert st == -8
