@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Throughput of the joint-sequence attention layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload full] [--no-cpu-baseline]
+
+One step is one pass of the whole layer over one batch of resident synthetic
+input: fused QKNorm + 3D RoPE (out of place, from the pristine q/k into working
+buffers, so every step sees the same input), block selection at the config's
+keep ratio, and block-sparse attention. K steps are timed between two device
+synchronisations. The kernels of each call are also bracketed by HIP events on
+the stream they run on, which gives the per-call averages.
+
+Printed (one JSON line): the metric (computed-tile attention TFLOP/s over the
+whole layer time), ms per layer, the per-call times, dense-equivalent
+TFLOP/s, the roofline of the dominant kernel (attention, MFMA-bound against the
+bf16 dense peak) and the fp64 CPU oracle's throughput on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+ATTN_SOURCE = os.path.join(ROOT, "sparse_attention_qknorm_amd", "csrc", "block_sparse_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_sparse_attn_full_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("block_sparse_attn.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "sparse_attention_qknorm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def computed_flops(mask, S: int, block: int, D: int) -> float:
+    """4*D*sum over kept (i, j) of n_i*n_j, from the actual mask (torch uint8 [B,H,nB,nB] on device)."""
+    import torch
+    nB = mask.shape[-1]
+    n = torch.full((nB,), float(block), dtype=torch.float64, device=mask.device)
+    n[-1] = float(S - block * (nB - 1))
+    m = (mask != 0).to(torch.float64)
+    return float(4.0 * D * torch.einsum("bhij,i,j->", m, n, n).item())
+
+
+def measured_traffic(kernel_hash: str, steps_launches: int):
+    """HBM bytes per attention launch from the committed counter runs, if they match this kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, cfg, keep: float, budget_s: float) -> dict:
+    """The fp64 oracle on a bounded sample of the same layer, scaled to computed TFLOP/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:                                   # pragma: no cover - threadpoolctl missing
+        threads = 1
+    S, H, D, block, nB = cfg.S, cfg.H, cfg.D, cfg.block, cfg.nB
+    h = 0
+    t0 = time.perf_counter()
+    q0 = inp["q"][:, :, h:h + 1].double().numpy()
+    k0 = inp["k"][:, :, h:h + 1].double().numpy()
+    qh, kh = oracle.qknorm_rope(q0, k0, inp["pos_thw"].numpy(), inp["w_q"].numpy(), inp["w_k"].numpy(),
+                                cfg.sections, cfg.rope_base, cfg.eps)
+    t_pro = time.perf_counter() - t0
+    import torch
+    qb = torch.from_numpy(qh.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    kb = torch.from_numpy(kh.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    t0 = time.perf_counter()
+    mask = oracle.select_blocks(qb, kb, block, keep)
+    t_sel = time.perf_counter() - t0
+    v0 = inp["v"][:, :, h:h + 1].double().numpy()
+    kk = oracle.num_kept_blocks(keep, nB)
+    rng = np.random.Generator(np.random.PCG64(99))
+    order = rng.permutation(nB)
+    t0 = time.perf_counter()
+    done = 0
+    flops = 0.0
+    last_n = S - block * (nB - 1)
+    sizes = np.full(nB, block, dtype=np.float64)
+    sizes[-1] = last_n
+    while done < nB and (time.perf_counter() - t0) < budget_s:
+        i = int(order[done])
+        oracle.block_sparse_attention_rows(qb, kb, v0, mask, block, [(0, 0, i)])
+        flops += 4.0 * D * sizes[i] * float(sizes[mask[0, 0, i] != 0].sum())
+        done += 1
+    t_att = time.perf_counter() - t0
+    # per-layer estimate: every head costs the same prologue and selection; attention scales by FLOPs
+    att_rate = flops / t_att
+    layer_flops = 4.0 * D * H * float((sizes[None, :] * sizes[:, None] * (mask[0, 0] != 0)).sum())
+    layer_s = H * (t_pro + t_sel) + layer_flops / att_rate
+    return {
+        "value": float(layer_flops / layer_s / 1e12),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "ms_per_layer_est": float(layer_s * 1e3),
+        "sample": (f"head 0 of the {cfg.name} layer: prologue over all {S} tokens ({t_pro:.2f} s), selection over "
+                   f"all {nB} query blocks ({t_sel:.2f} s), attention on {done} seeded-random query blocks of {nB} "
+                   f"({t_att:.2f} s, k={kk}); scaled to {H} heads. host: {platform.processor() or platform.machine()}, "
+                   f"{len(os.sched_getaffinity(0))} cpus visible, BLAS threads {threads}"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="full", choices=["full", "medium", "small", "tiny"])
+    ap.add_argument("--keep", type=float, default=None, help="keep ratio (default: the config's first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention in the CPU sample")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer would shard by "
+              "heads; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sparse_attention_qknorm_amd as saq
+    from sparse_attention_qknorm_amd import synth
+
+    cfg = synth.get_config(args.workload)
+    keep = args.keep if args.keep is not None else cfg.keep_ratios[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    saq.lib()
+
+    log(f"[bench] generating {cfg.name} inputs: B={cfg.B} S={cfg.S} H={cfg.H} D={cfg.D} block={cfg.block} keep={keep}")
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(cfg)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    q0, k0, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    pos, wq, wk = inp["pos_thw"].to(dev), inp["w_q"].to(dev), inp["w_k"].to(dev)
+    qh, kh = torch.empty_like(q0), torch.empty_like(k0)
+    nB = cfg.nB
+    mask = torch.empty((cfg.B, cfg.H, nB, nB), dtype=torch.uint8, device=dev)
+    ws = torch.empty(saq.select_workspace_bytes(cfg.B, cfg.S, cfg.H, cfg.D, cfg.block), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(q0)
+    stream = torch.cuda.current_stream(dev)
+
+    ev = {name: [] for name in ("pro", "sel", "att")}
+
+    def step(record: bool):
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+        saq.qknorm_rope_out(q0, k0, qh, kh, pos, (wq, wk), cfg.sections, cfg.rope_base, cfg.eps)
+        if record:
+            e[1].record(stream)
+        saq.select_blocks(qh, kh, keep, cfg.block, out=mask, workspace=ws)
+        if record:
+            e[2].record(stream)
+        saq.block_sparse_attn(qh, kh, v, mask, cfg.block, out=o)
+        if record:
+            e[3].record(stream)
+            ev["pro"].append((e[0], e[1]))
+            ev["sel"].append((e[1], e[2]))
+            ev["att"].append((e[2], e[3]))
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    flops = computed_flops(mask, cfg.S, cfg.block, cfg.D)
+    dense_flops = 4.0 * cfg.D * cfg.H * cfg.B * float(cfg.S) ** 2
+
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    def avg_ms(name):
+        return float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
+
+    ms = {n: avg_ms(n) for n in ev}
+    att_s = ms["att"] / 1e3
+    achieved = flops / att_s / 1e12
+    khash = attn_source_hash()
+    traffic = measured_traffic(khash, args.steps)
+    pro_bytes = 8.0 * cfg.D * cfg.H * cfg.B * cfg.S + 12.0 * cfg.S
+    sel_bytes = 4.0 * cfg.D * cfg.H * cfg.B * cfg.S
+
+    result = {
+        "metric": "joint-seq attention TFLOP/s + ms/layer (1 MI355X), % of bf16 MFMA peak",
+        "value": flops / (ms_step / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: one joint video+audio self-attention layer, B={cfg.B}, "
+                               f"S={cfg.S} ({cfg.T}x{cfg.Hg}x{cfg.W} video + {cfg.A} audio tokens), H={cfg.H}, "
+                               f"D={cfg.D}, block={cfg.block}, keep_ratio={keep}",
+                   "global_batch": cfg.B, "seq_len": cfg.S, "heads": cfg.H, "head_dim": cfg.D,
+                   "block": cfg.block, "keep_ratio": keep, "kept_blocks_per_row": saq.kept_blocks(keep, nB),
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_layer": ms_step,
+        "ms_per_call": {"qknorm_rope": ms["pro"], "select_blocks": ms["sel"], "block_sparse_attn": ms["att"]},
+        "attention_tflops_computed": achieved,
+        "attention_tflops_dense_equivalent": dense_flops / att_s / 1e12,
+        "layer_tflops_dense_equivalent": dense_flops / (ms_step / 1e3) / 1e12,
+        "attention_frac_of_bf16_peak": achieved / BF16_PEAK_TFLOPS,
+        "computed_tflop_per_layer": flops / 1e12,
+        "prologue_gbs": pro_bytes / (ms["pro"] / 1e3) / 1e9,
+        "select_pool_read_gbs": sel_bytes / (ms["sel"] / 1e3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic,
+                     "kernel": "d128::attn_kernel (block 128, head_dim 128)", "kernel_hash": khash,
+                     "flop_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s of attention)")
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, keep, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

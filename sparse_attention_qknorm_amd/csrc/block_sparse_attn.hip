@@ -245,6 +245,262 @@ __global__ __launch_bounds__(BLOCK * 2) void block_sparse_attn_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Production shape (block 128, head_dim 128): direct-to-LDS staging.
+//
+// K and V tiles (128 keys x 256 B) go from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds: no registers, asynchronous, and rows past S
+// read as zeros through the buffer's range check. Each 16-byte chunk c of LDS
+// row r sits at chunk position c ^ swz(r), an XOR swizzle under which both the
+// 16-byte K reads (16 rows, one chunk) and the transposed V reads (4 rows x 4
+// chunks) hit all 64 banks once.
+//
+// QK^T: lane (l32, g) reads K row pi(l32), pi swapping bits 2 and 3 of the row
+// index, so accumulator v of 32-key tile kt holds key
+// 32kt + 16(v/8) + 8g + 4((v/4)%2) + v%4: for 16-key step s = 2kt + a the
+// registers 8a..8a+7 are exactly keys 16s + 8g + 0..7, the B operand of the PV
+// MFMA in natural key order.
+// PV: V^T is read with ds_read_b64_tr_b16. Within each 16-lane group, lane j
+// supplies the 8 bytes at row kappa0 + j/4, columns d0 + 4(j%4); lane i then
+// receives V[kappa0 + e][d0 + i] for e = 0..3. Two such reads give a lane its
+// 8 keys for one d.
+// Softmax in the log2 domain with a lazily updated maximum: the running max
+// used in the exponent only moves (and O is only rescaled) when a tile's max
+// exceeds it by more than 8, so p <= 2^8 and the rescale is almost never paid.
+// Row sums use v_dot2 on the bf16 P, the same values the PV product consumes.
+namespace d128 {
+
+constexpr int kBlock = 128;
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kD * 2;
+constexpr int kTileBytes = kBlock * kRowBytes;               // 32 KB
+constexpr int kLoadsPerWave = kTileBytes / 1024 / (kThreads / kWave);   // 8 x 1 KB per wave per tile
+constexpr float kLazyRescale = 8.0f;                         // log2 units
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// s_waitcnt with vmcnt <= n and the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint8_t* __restrict__ mask, uint16_t* __restrict__ o, int32_t S, int32_t H, int32_t nB,
+    int64_t n_items, float scale_log2, uint32_t head_bytes) {
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[kTileBytes];
+    __shared__ uint16_t kept[kMaxBlocks];
+    __shared__ int n_kept_s;
+
+    const int64_t item = xcd_contiguous_index(blockIdx.x, n_items);
+    const int i = (int)(item % nB);
+    const int64_t bh = item / nB;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int l32 = lane % 32;
+    const int g = lane / 32;
+
+    if (wave == 0) {
+        const uint8_t* mrow = mask + item * (int64_t)nB;
+        int count = 0;
+        for (int j0 = 0; j0 < nB; j0 += kWave) {
+            const int j = j0 + lane;
+            const bool keep = j < nB && mrow[j] != 0;
+            const uint64_t bits = __ballot(keep);
+            if (keep) kept[count + __popcll(bits & ((1ull << lane) - 1ull))] = (uint16_t)j;
+            count += __popcll(bits);
+        }
+        if (lane == 0) n_kept_s = count;
+    }
+
+    const int64_t row_stride = (int64_t)H * kD;                 // elements
+    const uint32_t row_bytes_g = (uint32_t)(row_stride * 2);    // bytes between tokens
+    const int64_t head_off = b * (int64_t)S * row_stride + (int64_t)h * kD;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + head_off), (short)0,
+                                                                         (int)head_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), (short)0,
+                                                                         (int)head_bytes, 0x00020000);
+
+    // staging: load n of this wave fills LDS bytes [C*1024, C*1024+1024), C = 8*wave + n,
+    // i.e. rows 4C .. 4C+3; lane -> row 4C + lane/16 (row mod 16 = 4(n%4) + lane/16), chunk
+    // position lane%16, which holds global chunk (lane%16) ^ swz(row)
+    const uint32_t stage_row = (uint32_t)(4 * kLoadsPerWave * wave + lane / 16) * row_bytes_g;
+    uint32_t stage_chunk[4];
+#pragma unroll
+    for (int n4 = 0; n4 < 4; ++n4) stage_chunk[n4] = (uint32_t)(((lane % 16) ^ (((lane / 16) << 2) | n4)) * 16);
+    auto issue = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint8_t* dst, int j) {
+        const uint32_t tile_off = (uint32_t)j * (uint32_t)kBlock * row_bytes_g;
+#pragma unroll
+        for (int n = 0; n < kLoadsPerWave; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (lds_void*)(dst + (kLoadsPerWave * wave + n) * 1024), 16,
+                (int)(stage_row + stage_chunk[n % 4] + tile_off + (uint32_t)(4 * n) * row_bytes_g), 0, 0, 0);
+    };
+
+    // Q^T as the B operand: row 32*wave + l32 of the block, d = 16*st + 8g + [0..7]
+    bf16x8 qb[kD / 16];
+    {
+        const int qrow = i * kBlock + wave * 32 + l32;
+        if (qrow < S) {
+            const uint16_t* src = q + head_off + (int64_t)qrow * row_stride + 8 * g;
+#pragma unroll
+            for (int st = 0; st < kD / 16; ++st) qb[st] = *(const bf16x8*)(src + 16 * st);
+        } else {
+#pragma unroll
+            for (int st = 0; st < kD / 16; ++st) qb[st] = (bf16x8){};
+        }
+    }
+
+    // LDS read addresses
+    const int krow = swap_bits23(l32);                 // K row this lane feeds as A-operand row l32
+    const int kfr = swz(krow);
+    const int grp = lane / 16;
+    const int jl = lane % 16;
+
+    f32x16 oacc[kD / 32];
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t) oacc[t] = (f32x16){};
+    float m_used = -INFINITY;
+    float l_run = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    __syncthreads();
+    const int n_kept = n_kept_s;
+    if (n_kept > 0) {
+        issue(rk, k_lds, kept[0]);
+        issue(rv, v_lds, kept[0]);
+    }
+
+    for (int n = 0; n < n_kept; ++n) {
+        const int j = kept[n];
+        const bool more = n + 1 < n_kept;
+        wait_vmcnt<kLoadsPerWave>();                  // K_n landed (V_n may still be in flight)
+        __syncthreads();
+
+        f32x16 sacc[kBlock / 32];
+#pragma unroll
+        for (int kt = 0; kt < kBlock / 32; ++kt) sacc[kt] = (f32x16){};
+        const uint8_t* krow_p = k_lds + krow * kRowBytes;
+#pragma unroll
+        for (int st = 0; st < kD / 16; ++st) {
+            const int c = (2 * st + g) ^ kfr;
+#pragma unroll
+            for (int kt = 0; kt < kBlock / 32; ++kt) {      // four independent accumulators in turn
+                const bf16x8 a = *(const bf16x8*)(krow_p + kt * 32 * kRowBytes + c * 16);
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[st], sacc[kt], 0, 0, 0);
+            }
+        }
+        __syncthreads();                               // every wave is done with K_n
+        if (more) issue(rk, k_lds, kept[n + 1]);
+
+        // ---- softmax
+        if ((j + 1) * kBlock > S) {                    // ragged last block: keys past S take no part
+#pragma unroll
+            for (int kt = 0; kt < kBlock / 32; ++kt)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const int key = j * kBlock + 32 * kt + 16 * (vv / 8) + 8 * g + 4 * ((vv / 4) % 2) + vv % 4;
+                    if (key >= S) sacc[kt][vv] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < kBlock / 32; ++kt)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) mx = fmaxf(mx, sacc[kt][vv]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * scale_log2;
+        const bool grow = mt > m_used + kLazyRescale;
+        if (__ballot(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_used - mt) : 1.0f;
+            m_used = grow ? mt : m_used;
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < kD / 32; ++t) oacc[t] *= alpha;
+        }
+        bf16x8 pb[kBlock / 16];
+#pragma unroll
+        for (int s = 0; s < kBlock / 16; ++s) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pb[s][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[s / 2][8 * (s % 2) + e], scale_log2, -m_used));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2 t2 = {pb[s][2 * e], pb[s][2 * e + 1]};
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(t2, ones, l_run, false);
+            }
+        }
+
+        // ---- O^T += V^T P^T
+        if (more) wait_vmcnt<kLoadsPerWave>();         // V_n landed; K_{n+1} may be in flight
+        else wait_vmcnt<0>();
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < kBlock / 16; ++s) {
+#pragma unroll
+            for (int t = 0; t < kD / 32; ++t) {              // four independent accumulators in turn
+                bf16x4 half[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r = 16 * s + 8 * g + 4 * hh + jl / 4;
+                    const int c = 4 * t + 2 * (grp % 2) + (jl % 4) / 2;
+                    const uint8_t* p = v_lds + r * kRowBytes + ((c ^ swz(r)) * 16) + 8 * (jl % 2);
+                    half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+                }
+                const bf16x8 a = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], oacc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();                               // every wave is done with V_n
+        if (more) issue(rv, v_lds, kept[n + 1]);
+    }
+
+    // ---- normalise and store: lane holds row l32 and d = 32t + 8(v/4) + 4g + v%4
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const int qrow = i * kBlock + wave * 32 + l32;
+    if (qrow < S) {
+        uint16_t* dst = o + head_off + (int64_t)qrow * row_stride;
+#pragma unroll
+        for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                uint2 w;
+                w.x = f32_to_bf16_bits(oacc[t][4 * m + 0] * inv) | (f32_to_bf16_bits(oacc[t][4 * m + 1] * inv) << 16);
+                w.y = f32_to_bf16_bits(oacc[t][4 * m + 2] * inv) | (f32_to_bf16_bits(oacc[t][4 * m + 3] * inv) << 16);
+                *(uint2*)(dst + t * 32 + 8 * m + 4 * g) = w;
+            }
+    }
+}
+
+hipError_t launch(const void* q, const void* k, const void* v, const uint8_t* mask, int32_t B, int32_t S, int32_t H,
+                  float scale, void* o, hipStream_t stream) {
+    const int32_t nB = (S + kBlock - 1) / kBlock;
+    const int64_t n_items = (int64_t)B * H * nB;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    // bytes of one head's rows within one batch entry, up to the end of row S-1
+    const uint64_t head_bytes = ((uint64_t)(S - 1) * H * kD + kD) * 2;
+    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, stream, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, mask, (uint16_t*)o, S, H, nB, n_items, scale_log2,
+                       (uint32_t)head_bytes);
+    return hipGetLastError();
+}
+
+}  // namespace d128
+
 template <int BLOCK, int D>
 hipError_t launch_impl(const void* q, const void* k, const void* v, const uint8_t* mask, int32_t B, int32_t S,
                        int32_t H, float scale, void* o, hipStream_t stream) {
@@ -263,7 +519,7 @@ hipError_t launch_impl(const void* q, const void* k, const void* v, const uint8_
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* mask,
                                     int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
                                     float scale, void* o, hipStream_t stream) {
-    if (block == 128 && D == 128) return launch_impl<128, 128>(q, k, v, mask, B, S, H, scale, o, stream);
+    if (block == 128 && D == 128) return d128::launch(q, k, v, mask, B, S, H, scale, o, stream);
     if (block == 128 && D == 64) return launch_impl<128, 64>(q, k, v, mask, B, S, H, scale, o, stream);
     if (block == 64 && D == 128) return launch_impl<64, 128>(q, k, v, mask, B, S, H, scale, o, stream);
     return launch_impl<64, 64>(q, k, v, mask, B, S, H, scale, o, stream);
