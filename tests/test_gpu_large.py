@@ -1,0 +1,189 @@
+"""GPU parity at the medium, full (127,040-token) and sweep sizes, in the launch
+configuration the bench times (block 128, head_dim 128).
+
+The oracle cannot redo a whole full-size layer in seconds, so it checks
+samples: prologue rows of selected tokens, masks of selected heads (bit-exact,
+from the GPU's own bf16 q_hat/k_hat), and attention outputs of selected query
+blocks (first, last/partial, the block that mixes video and audio, audio
+blocks, seeded random ones). Properties that hold at any size are checked on
+every output: finite, and inside the per-(head, channel) range of V.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_qknorm_amd as saq
+from sparse_attention_qknorm_amd import synth
+from parity_tools import check_attention, check_prologue, log, oracle_mask, pooled_exactness_ok, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+class Layer:
+    """One layer's inputs on host and device, and the GPU path's outputs."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        self.cfg = inp["cfg"]
+        g = {n: inp[n].to(DEV) for n in ("q", "k", "v", "pos_thw", "w_q", "w_k")}
+        self.v = g["v"]
+        self.qh, self.kh = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+        c = self.cfg
+        saq.qknorm_rope_out(g["q"], g["k"], self.qh, self.kh, g["pos_thw"], (g["w_q"], g["w_k"]), c.sections,
+                            c.rope_base, c.eps)
+        torch.cuda.synchronize()
+        self.qh64_cache = None
+
+    def run(self, keep):
+        c = self.cfg
+        mask = saq.select_blocks(self.qh, self.kh, keep, c.block)
+        o = saq.block_sparse_attn(self.qh, self.kh, self.v, mask, c.block)
+        torch.cuda.synchronize()
+        return mask, o
+
+    def host_qk(self):
+        if self.qh64_cache is None:
+            self.qh64_cache = (self.qh.cpu(), self.kh.cpu())
+        return self.qh64_cache
+
+
+def _sample_tokens(cfg, n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fixed = [0, 1, cfg.block - 1, cfg.block, cfg.S_video - 1, cfg.S_video, cfg.S - 1]
+    return np.unique(np.concatenate([fixed, rng.integers(0, cfg.S, n)]))
+
+
+def _check_prologue_sample(layer, seed):
+    cfg, inp = layer.cfg, layer.inp
+    toks = _sample_tokens(cfg, 1500, seed)
+    qh, kh = layer.host_qk()
+    rq, rk = oracle.qknorm_rope(to64(inp["q"][:, toks]), to64(inp["k"][:, toks]), inp["pos_thw"].numpy()[toks],
+                                inp["w_q"].numpy(), inp["w_k"].numpy(), cfg.sections, cfg.rope_base, cfg.eps)
+    fq = check_prologue(to64(qh[:, toks]), rq, f"{cfg.name} q_hat ({len(toks)} tokens)")
+    fk = check_prologue(to64(kh[:, toks]), rk, f"{cfg.name} k_hat ({len(toks)} tokens)")
+    log(f"  {cfg.name} prologue on {len(toks)} sampled tokens: RNE-exact fraction q {fq:.4f} k {fk:.4f}")
+
+
+def _check_masks(layer, mask, keep, heads):
+    cfg = layer.cfg
+    qh, kh = layer.host_qk()
+    m_gpu = mask.cpu().numpy()
+    kk = saq.kept_blocks(keep, cfg.nB)
+    assert (m_gpu.sum(axis=-1) == kk).all() and (np.diagonal(m_gpu, axis1=2, axis2=3) == 1).all()
+    for h in heads:
+        q64 = qh[:, :, h:h + 1].double().numpy()
+        k64 = kh[:, :, h:h + 1].double().numpy()
+        assert pooled_exactness_ok(q64) and pooled_exactness_ok(k64)
+        ref = oracle_mask(q64, k64, cfg.block, keep)[(0, 0)]
+        assert np.array_equal(m_gpu[0, h], ref), f"{cfg.name} keep={keep}: mask differs on head {h}"
+    log(f"  {cfg.name} keep={keep}: masks bit-exact on heads {list(heads)}; k={kk} per row everywhere")
+    return m_gpu
+
+
+def _check_attention_sample(layer, m_gpu, o, rows, what):
+    cfg = layer.cfg
+    qh, kh = layer.host_qk()
+    S, block = cfg.S, cfg.block
+    heads = sorted({h for _, h, _ in rows})
+    got = []
+    refs = []
+    for h in heads:
+        hr = [(b, 0, i) for (b, hh, i) in rows if hh == h]
+        q64 = qh[:, :, h:h + 1].double().numpy()
+        k64 = kh[:, :, h:h + 1].double().numpy()
+        v64 = layer.inp["v"][:, :, h:h + 1].double().numpy()
+        refs.append(oracle.block_sparse_attention_rows(q64, k64, v64, m_gpu[:, h:h + 1], block, hr))
+        for (b, _, i) in hr:
+            blk = np.zeros((block, cfg.D))
+            hi = min(S, (i + 1) * block)
+            blk[:hi - i * block] = to64(o[b, i * block:hi, h])
+            got.append(blk)
+    check_attention(np.stack(got), np.concatenate(refs), f"{what} ({len(rows)} query blocks)")
+
+
+def _check_properties(layer, o):
+    # any size: finite, and each output channel inside [min, max] of that head's V channel
+    assert torch.isfinite(o.float()).all()
+    vmin = layer.v.float().amin(dim=1, keepdim=True)
+    vmax = layer.v.float().amax(dim=1, keepdim=True)
+    of = o.float()
+    slack = 2e-2
+    assert bool(((of >= vmin - slack) & (of <= vmax + slack)).all())
+
+
+def _rows(cfg, n, seed, heads):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nB = cfg.nB
+    audio0 = cfg.S_video // cfg.block
+    fixed = [0, nB - 1, audio0, min(nB - 1, audio0 + 1), nB // 2]
+    rows = []
+    for h in heads:
+        for i in fixed:
+            rows.append((0, h, int(i)))
+    for _ in range(n):
+        rows.append((0, int(rng.choice(heads)), int(rng.integers(0, nB))))
+    return sorted(set(rows))
+
+
+@pytest.fixture(scope="module")
+def medium():
+    log("[medium] generating inputs")
+    return Layer(synth.make_inputs("medium"))
+
+
+@pytest.mark.timeout(300)
+def test_medium_prologue_sampled(medium):
+    _check_prologue_sample(medium, 1)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("keep", [0.2, 1.0])
+def test_medium_select_and_attention(medium, keep):
+    mask, o = medium.run(keep)
+    if keep == 1.0:
+        assert bool((mask == 1).all())
+        m_gpu = mask.cpu().numpy()
+    else:
+        m_gpu = _check_masks(medium, mask, keep, range(medium.cfg.H))
+    _check_properties(medium, o)
+    _check_attention_sample(medium, m_gpu, o, _rows(medium.cfg, 16, 2, [0, 7, 23]), f"medium keep={keep} o")
+
+
+@pytest.fixture(scope="module")
+def full():
+    log("[full] generating inputs (127040 tokens x 40 heads)")
+    return Layer(synth.make_inputs("full"))
+
+
+@pytest.mark.timeout(300)
+def test_full_prologue_sampled(full):
+    _check_prologue_sample(full, 3)
+
+
+@pytest.mark.timeout(300)
+def test_full_select_and_attention(full):
+    keep = full.cfg.keep_ratios[0]
+    mask, o = full.run(keep)
+    m_gpu = _check_masks(full, mask, keep, [0, 13, 39])
+    _check_properties(full, o)
+    _check_attention_sample(full, m_gpu, o, _rows(full.cfg, 6, 4, [0, 39]), "full keep=0.15 o")
+    # the same launch twice gives the same bytes
+    mask2, o2 = full.run(keep)
+    assert torch.equal(mask, mask2) and torch.equal(o, o2)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("step", [1, 7])
+def test_sweep_step(step):
+    cfg = synth.get_config("sweep")
+    log(f"[sweep] generating step {step}")
+    layer = Layer(synth.make_sweep_inputs(cfg, step))
+    for keep in (0.1, 0.3):
+        mask, o = layer.run(keep)
+        m_gpu = _check_masks(layer, mask, keep, [5])
+        if keep == 0.3:
+            _check_properties(layer, o)
+            _check_attention_sample(layer, m_gpu, o, [(0, 5, 0), (0, 5, 976), (0, 5, 992), (0, 5, 500)],
+                                    f"sweep step {step} keep={keep} o")
