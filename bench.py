@@ -137,6 +137,9 @@ def main(argv=None) -> int:
     ap.add_argument("--keep", type=float, default=None, help="keep ratio (default: the config's first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention in the CPU sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB read + 1 GiB write elementwise copy (3 launches) after the timed "
+                         "steps, as the reference kernel for scaling HBM byte counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -248,6 +251,14 @@ def main(argv=None) -> int:
                      "kernel": "d128::attn_kernel (block 128, head_dim 128)", "kernel_hash": khash,
                      "flop_per_launch": flops},
     }
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 3,
+                                      "kernel": "torch elementwise mul by 1.0 (fp32)"}
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s of attention)")
         result["cpu_baseline"] = cpu_baseline(inp, cfg, keep, args.cpu_budget)

@@ -292,47 +292,22 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint8_t* __restrict__ mask, uint16_t* __restrict__ o, int32_t S, int32_t H, int32_t nB,
-    int64_t n_items, float scale_log2, uint32_t head_bytes) {
-    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[kTileBytes];
-    __shared__ uint16_t kept[kMaxBlocks];
-    __shared__ int n_kept_s;
-
-    const int64_t item = xcd_contiguous_index(blockIdx.x, n_items);
-    const int i = (int)(item % nB);
-    const int64_t bh = item / nB;
-    const int h = (int)(bh % H);
-    const int64_t b = bh / H;
-
+// The tile loop. The two LDS tiles come in as separate __restrict__ pointers:
+// once inlined, the compiler's wait-count pass can then tell the K and V
+// direct-to-LDS copies apart, so reading V waits only for V's copy and not for
+// the K prefetch of the next tile issued just before.
+__device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* __restrict__ v_lds,
+                                          const uint16_t* __restrict__ kept, int n_kept,
+                                          const __amdgpu_buffer_rsrc_t& rk, const __amdgpu_buffer_rsrc_t& rv,
+                                          uint32_t row_bytes_g, const bf16x8 (&qb)[kD / 16], int32_t S,
+                                          float scale_log2, f32x16 (&oacc)[kD / 32], float& l_run) {
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const int l32 = lane % 32;
     const int g = lane / 32;
-
-    if (wave == 0) {
-        const uint8_t* mrow = mask + item * (int64_t)nB;
-        int count = 0;
-        for (int j0 = 0; j0 < nB; j0 += kWave) {
-            const int j = j0 + lane;
-            const bool keep = j < nB && mrow[j] != 0;
-            const uint64_t bits = __ballot(keep);
-            if (keep) kept[count + __popcll(bits & ((1ull << lane) - 1ull))] = (uint16_t)j;
-            count += __popcll(bits);
-        }
-        if (lane == 0) n_kept_s = count;
-    }
-
-    const int64_t row_stride = (int64_t)H * kD;                 // elements
-    const uint32_t row_bytes_g = (uint32_t)(row_stride * 2);    // bytes between tokens
-    const int64_t head_off = b * (int64_t)S * row_stride + (int64_t)h * kD;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + head_off), (short)0,
-                                                                         (int)head_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), (short)0,
-                                                                         (int)head_bytes, 0x00020000);
+    const int grp = lane / 16;
+    const int jl = lane % 16;
 
     // staging: load n of this wave fills LDS bytes [C*1024, C*1024+1024), C = 8*wave + n,
     // i.e. rows 4C .. 4C+3; lane -> row 4C + lane/16 (row mod 16 = 4(n%4) + lane/16), chunk
@@ -341,49 +316,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     uint32_t stage_chunk[4];
 #pragma unroll
     for (int n4 = 0; n4 < 4; ++n4) stage_chunk[n4] = (uint32_t)(((lane % 16) ^ (((lane / 16) << 2) | n4)) * 16);
-    auto issue = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint8_t* dst, int j) {
+    auto issue_k = [&](int j) {
         const uint32_t tile_off = (uint32_t)j * (uint32_t)kBlock * row_bytes_g;
 #pragma unroll
         for (int n = 0; n < kLoadsPerWave; ++n)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (lds_void*)(dst + (kLoadsPerWave * wave + n) * 1024), 16,
+                rk, (lds_void*)(k_lds + (kLoadsPerWave * wave + n) * 1024), 16,
+                (int)(stage_row + stage_chunk[n % 4] + tile_off + (uint32_t)(4 * n) * row_bytes_g), 0, 0, 0);
+    };
+    auto issue_v = [&](int j) {
+        const uint32_t tile_off = (uint32_t)j * (uint32_t)kBlock * row_bytes_g;
+#pragma unroll
+        for (int n = 0; n < kLoadsPerWave; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (lds_void*)(v_lds + (kLoadsPerWave * wave + n) * 1024), 16,
                 (int)(stage_row + stage_chunk[n % 4] + tile_off + (uint32_t)(4 * n) * row_bytes_g), 0, 0, 0);
     };
 
-    // Q^T as the B operand: row 32*wave + l32 of the block, d = 16*st + 8g + [0..7]
-    bf16x8 qb[kD / 16];
-    {
-        const int qrow = i * kBlock + wave * 32 + l32;
-        if (qrow < S) {
-            const uint16_t* src = q + head_off + (int64_t)qrow * row_stride + 8 * g;
-#pragma unroll
-            for (int st = 0; st < kD / 16; ++st) qb[st] = *(const bf16x8*)(src + 16 * st);
-        } else {
-#pragma unroll
-            for (int st = 0; st < kD / 16; ++st) qb[st] = (bf16x8){};
-        }
-    }
-
-    // LDS read addresses
     const int krow = swap_bits23(l32);                 // K row this lane feeds as A-operand row l32
     const int kfr = swz(krow);
-    const int grp = lane / 16;
-    const int jl = lane % 16;
-
-    f32x16 oacc[kD / 32];
-#pragma unroll
-    for (int t = 0; t < kD / 32; ++t) oacc[t] = (f32x16){};
     float m_used = -INFINITY;
-    float l_run = 0.f;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    __syncthreads();
-    const int n_kept = n_kept_s;
     if (n_kept > 0) {
-        issue(rk, k_lds, kept[0]);
-        issue(rv, v_lds, kept[0]);
+        issue_k(kept[0]);
+        issue_v(kept[0]);
     }
-
     for (int n = 0; n < n_kept; ++n) {
         const int j = kept[n];
         const bool more = n + 1 < n_kept;
@@ -404,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
             }
         }
         __syncthreads();                               // every wave is done with K_n
-        if (more) issue(rk, k_lds, kept[n + 1]);
+        if (more) issue_k(kept[n + 1]);
 
         // ---- softmax
         if ((j + 1) * kBlock > S) {                    // ragged last block: keys past S take no part
@@ -465,13 +423,82 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
             }
         }
         __syncthreads();                               // every wave is done with V_n
-        if (more) issue(rv, v_lds, kept[n + 1]);
+        if (more) issue_v(kept[n + 1]);
     }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint8_t* __restrict__ mask, uint16_t* __restrict__ o, int32_t S, int32_t H, int32_t nB,
+    int64_t n_items, float scale_log2, uint32_t head_bytes) {
+    __shared__ __attribute__((aligned(1024))) uint8_t k_lds[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t v_lds[kTileBytes];
+    __shared__ uint16_t kept[kMaxBlocks];
+    __shared__ int n_kept_s;
+
+    // Hardware deals workgroup ids round-robin over the 8 XCDs. Give XCD x the query
+    // blocks [x*per, (x+1)*per) of every (b, h) in turn, so at any moment all XCDs work on
+    // the same head (one head's K and V stay resident in the memory-side cache) and each
+    // XCD's L2 serves adjacent query blocks, whose kept key blocks overlap.
+    const int per = (nB + kNumXcd - 1) / kNumXcd;
+    const int64_t slot = blockIdx.x / kNumXcd;
+    const int i = (int)(blockIdx.x % kNumXcd) * per + (int)(slot % per);
+    if (i >= nB) return;                               // ragged split: whole workgroup leaves
+    const int64_t bh = slot / per;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int64_t item = bh * nB + i;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int l32 = lane % 32;
+    const int g = lane / 32;
+
+    if (wave == 0) {
+        const uint8_t* mrow = mask + item * (int64_t)nB;
+        int count = 0;
+        for (int j0 = 0; j0 < nB; j0 += kWave) {
+            const int j = j0 + lane;
+            const bool keep = j < nB && mrow[j] != 0;
+            const uint64_t bits = __ballot(keep);
+            if (keep) kept[count + __popcll(bits & ((1ull << lane) - 1ull))] = (uint16_t)j;
+            count += __popcll(bits);
+        }
+        if (lane == 0) n_kept_s = count;
+    }
+
+    const int64_t row_stride = (int64_t)H * kD;                 // elements
+    const uint32_t row_bytes_g = (uint32_t)(row_stride * 2);    // bytes between tokens
+    const int64_t head_off = b * (int64_t)S * row_stride + (int64_t)h * kD;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + head_off), (short)0,
+                                                                         (int)head_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + head_off), (short)0,
+                                                                         (int)head_bytes, 0x00020000);
+
+    // Q^T as the B operand: row 32*wave + l32 of the block, d = 16*st + 8g + [0..7]
+    bf16x8 qb[kD / 16];
+    const int qrow = i * kBlock + wave * 32 + l32;
+    if (qrow < S) {
+        const uint16_t* src = q + head_off + (int64_t)qrow * row_stride + 8 * g;
+#pragma unroll
+        for (int st = 0; st < kD / 16; ++st) qb[st] = *(const bf16x8*)(src + 16 * st);
+    } else {
+#pragma unroll
+        for (int st = 0; st < kD / 16; ++st) qb[st] = (bf16x8){};
+    }
+
+    f32x16 oacc[kD / 32];
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t) oacc[t] = (f32x16){};
+    float l_run = 0.f;
+
+    __syncthreads();
+    tile_loop(k_lds, v_lds, kept, n_kept_s, rk, rv, row_bytes_g, qb, S, scale_log2, oacc, l_run);
 
     // ---- normalise and store: lane holds row l32 and d = 32t + 8(v/4) + 4g + v%4
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const int qrow = i * kBlock + wave * 32 + l32;
     if (qrow < S) {
         uint16_t* dst = o + head_off + (int64_t)qrow * row_stride;
 #pragma unroll
@@ -490,10 +517,12 @@ hipError_t launch(const void* q, const void* k, const void* v, const uint8_t* ma
                   float scale, void* o, hipStream_t stream) {
     const int32_t nB = (S + kBlock - 1) / kBlock;
     const int64_t n_items = (int64_t)B * H * nB;
+    const int per = (nB + kNumXcd - 1) / kNumXcd;
+    const int64_t n_groups = (int64_t)B * H * per * kNumXcd;
     const float scale_log2 = scale * 1.4426950408889634f;
     // bytes of one head's rows within one batch entry, up to the end of row S-1
     const uint64_t head_bytes = ((uint64_t)(S - 1) * H * kD + kD) * 2;
-    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)n_items), dim3(kThreads), 0, stream, (const uint16_t*)q,
+    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)n_groups), dim3(kThreads), 0, stream, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, mask, (uint16_t*)o, S, H, nB, n_items, scale_log2,
                        (uint32_t)head_bytes);
     return hipGetLastError();
