@@ -135,6 +135,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="full", choices=["full", "medium", "small", "tiny"])
     ap.add_argument("--keep", type=float, default=None, help="keep ratio (default: the config's first)")
+    ap.add_argument("--path", default="fused", choices=["fused", "split"],
+                    help="fused: prologue with block pooling folded in, then selection from the pooled vectors; "
+                         "split: the three separate calls qknorm_rope / select_blocks / block_sparse_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention in the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -178,10 +181,17 @@ def main(argv=None) -> int:
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
-        saq.qknorm_rope_out(q0, k0, qh, kh, pos, (wq, wk), cfg.sections, cfg.rope_base, cfg.eps)
+        if args.path == "fused":
+            saq.qknorm_rope_pool(q0, k0, qh, kh, pos, (wq, wk), cfg.sections, cfg.rope_base, cfg.eps, cfg.block,
+                                 workspace=ws)
+        else:
+            saq.qknorm_rope_out(q0, k0, qh, kh, pos, (wq, wk), cfg.sections, cfg.rope_base, cfg.eps)
         if record:
             e[1].record(stream)
-        saq.select_blocks(qh, kh, keep, cfg.block, out=mask, workspace=ws)
+        if args.path == "fused":
+            saq.select_blocks_pooled(qh.shape, keep, ws, cfg.block, out=mask)
+        else:
+            saq.select_blocks(qh, kh, keep, cfg.block, out=mask, workspace=ws)
         if record:
             e[2].record(stream)
         saq.block_sparse_attn(qh, kh, v, mask, cfg.block, out=o)
@@ -216,7 +226,6 @@ def main(argv=None) -> int:
     khash = attn_source_hash()
     traffic = measured_traffic(khash, args.steps)
     pro_bytes = 8.0 * cfg.D * cfg.H * cfg.B * cfg.S + 12.0 * cfg.S
-    sel_bytes = 4.0 * cfg.D * cfg.H * cfg.B * cfg.S
 
     result = {
         "metric": "joint-seq attention TFLOP/s + ms/layer (1 MI355X), % of bf16 MFMA peak",
@@ -238,14 +247,16 @@ def main(argv=None) -> int:
                    "block": cfg.block, "keep_ratio": keep, "kept_blocks_per_row": saq.kept_blocks(keep, nB),
                    "parallelism": "none (1 GPU)"},
         "ms_per_layer": ms_step,
-        "ms_per_call": {"qknorm_rope": ms["pro"], "select_blocks": ms["sel"], "block_sparse_attn": ms["att"]},
+        "path": args.path,
+        "ms_per_call": ({"qknorm_rope_pool": ms["pro"], "select_blocks_pooled": ms["sel"],
+                         "block_sparse_attn": ms["att"]} if args.path == "fused" else
+                        {"qknorm_rope": ms["pro"], "select_blocks": ms["sel"], "block_sparse_attn": ms["att"]}),
         "attention_tflops_computed": achieved,
         "attention_tflops_dense_equivalent": dense_flops / att_s / 1e12,
         "layer_tflops_dense_equivalent": dense_flops / (ms_step / 1e3) / 1e12,
         "attention_frac_of_bf16_peak": achieved / BF16_PEAK_TFLOPS,
         "computed_tflop_per_layer": flops / 1e12,
         "prologue_gbs": pro_bytes / (ms["pro"] / 1e3) / 1e9,
-        "select_pool_read_gbs": sel_bytes / (ms["sel"] / 1e3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic,
                      "kernel": "d128::attn_kernel (block 128, head_dim 128)", "kernel_hash": khash,

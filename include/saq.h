@@ -142,6 +142,35 @@ int saq_block_sparse_attn(const void* q, const void* k, const void* v, const uin
                           int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
                           float softmax_scale, void* o, void* stream);
 
+/*
+ * Fused QKNorm + 3D RoPE + block pooling (the first step of selection folded
+ * into the prologue's single pass over Q and K; Sol Engine "H3 on device" page,
+ * fusion table "fused QKNorm + RoPE", and its Sol-Attn paragraph on avoiding a
+ * separate routing stage). Computes exactly what saq_qknorm_rope_out computes
+ * into q_out/k_out (same bits), and also writes the per-block fp64 means of the
+ * bf16 q_out and k_out into the head of `workspace`, as saq_select_blocks would
+ * compute them (bit-identical: the sums of bf16 values are exact in fp64).
+ * Follow with saq_select_blocks_pooled on the same workspace.
+ *
+ *   block      64 or 128; workspace >= saq_select_blocks_workspace_bytes(...),
+ *              256-byte aligned.
+ *   Extra limit: H*D <= 8192 (SAQ_ERR_UNSUPPORTED otherwise).
+ * Aliasing rules as saq_qknorm_rope_out; the workspace must not overlap any
+ * tensor.
+ */
+int saq_qknorm_rope_pool(const void* q_in, const void* k_in, void* q_out, void* k_out, const int32_t* pos_thw,
+                         const float* w_q, const float* w_k, int32_t B, int32_t S, int32_t H, int32_t D,
+                         int32_t dt, int32_t dh, int32_t dw, double rope_base, double eps, int32_t block,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block selection from the pooled vectors saq_qknorm_rope_pool left in
+ * `workspace` (scores + top-k + diagonal, the same rule and bit-identical result
+ * as saq_select_blocks on the tensors that call wrote).
+ */
+int saq_select_blocks_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, double keep_ratio,
+                             uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* saq_status_string(int status);
 

@@ -21,8 +21,8 @@ import torch
 
 from ._binding import SaqError, check, lib
 
-__all__ = ["qknorm_rope", "qknorm_rope_out", "select_blocks", "select_workspace_bytes", "block_sparse_attn",
-           "kept_blocks", "SaqError", "lib"]
+__all__ = ["qknorm_rope", "qknorm_rope_out", "qknorm_rope_pool", "select_blocks", "select_blocks_pooled",
+           "select_workspace_bytes", "block_sparse_attn", "kept_blocks", "SaqError", "lib"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -64,6 +64,56 @@ def qknorm_rope_out(q: torch.Tensor, k: torch.Tensor, q_out: torch.Tensor, k_out
                                    pos_thw.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), B, S, H, D, dt, dh, dw,
                                    float(base), float(eps), _stream(q))
     check(st, "saq_qknorm_rope_out")
+
+
+def _check_prologue_args(q, k, q_out, k_out, pos_thw, weights):
+    _check_qkv("q", q)
+    for n, t in (("k", k), ("q_out", q_out), ("k_out", k_out)):
+        _check_qkv(n, t, q)
+    B, S, H, D = q.shape
+    if pos_thw.dtype != torch.int32 or tuple(pos_thw.shape) != (S, 3) or not pos_thw.is_contiguous() \
+            or pos_thw.device != q.device:
+        raise ValueError("pos_thw must be a contiguous int32 [S,3] tensor on q's device")
+    for n, w in zip(("w_q", "w_k"), weights):
+        if w.dtype != torch.float32 or tuple(w.shape) != (D,) or not w.is_contiguous() or w.device != q.device:
+            raise ValueError(f"{n} must be a contiguous fp32 [D] tensor on q's device")
+
+
+def qknorm_rope_pool(q: torch.Tensor, k: torch.Tensor, q_out: torch.Tensor, k_out: torch.Tensor,
+                     pos_thw: torch.Tensor, weights: Tuple[torch.Tensor, torch.Tensor], sections: Sequence[int],
+                     base: float = 10000.0, eps: float = 1e-6, block: int = 128,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """QKNorm + 3D RoPE into (q_out, k_out) plus the per-block pooled means, written into the returned
+    selection workspace (saq_qknorm_rope_pool). Pass that workspace to select_blocks_pooled."""
+    _check_prologue_args(q, k, q_out, k_out, pos_thw, weights)
+    B, S, H, D = q.shape
+    need = select_workspace_bytes(B, S, H, D, block)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dt, dh, dw = (int(x) for x in sections)
+    w_q, w_k = weights
+    st = lib().saq_qknorm_rope_pool(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
+                                    pos_thw.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), B, S, H, D, dt, dh, dw,
+                                    float(base), float(eps), block, workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(q))
+    check(st, "saq_qknorm_rope_pool")
+    return workspace
+
+
+def select_blocks_pooled(shape: Sequence[int], keep_ratio: float, workspace: torch.Tensor, block: int = 128,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block mask from the pooled vectors qknorm_rope_pool left in `workspace` (saq_select_blocks_pooled).
+    shape = (B, S, H, D) of q."""
+    B, S, H, D = (int(x) for x in shape)
+    nB = -(-S // block)
+    if out is None:
+        out = torch.empty((B, H, nB, nB), dtype=torch.uint8, device=workspace.device)
+    elif out.dtype != torch.uint8 or tuple(out.shape) != (B, H, nB, nB) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 [B,H,nB,nB] tensor")
+    st = lib().saq_select_blocks_pooled(B, S, H, D, block, float(keep_ratio), out.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(workspace))
+    check(st, "saq_select_blocks_pooled")
+    return out
 
 
 def kept_blocks(keep_ratio: float, nB: int) -> int:

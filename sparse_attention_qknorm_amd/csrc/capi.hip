@@ -106,6 +106,51 @@ int saq_qknorm_rope(void* q, void* k, const int32_t* pos_thw, const float* w_q, 
     return saq_qknorm_rope_out(q, k, q, k, pos_thw, w_q, w_k, B, S, H, D, dt, dh, dw, rope_base, eps, stream);
 }
 
+int saq_qknorm_rope_pool(const void* q_in, const void* k_in, void* q_out, void* k_out, const int32_t* pos_thw,
+                         const float* w_q, const float* w_k, int32_t B, int32_t S, int32_t H, int32_t D,
+                         int32_t dt, int32_t dh, int32_t dw, double rope_base, double eps, int32_t block,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    int st = validate_prologue(q_in, k_in, q_out, k_out, pos_thw, w_q, w_k, B, S, H, D, dt, dh, dw, rope_base, eps);
+    if (st) return st;
+    st = check_block(S, block);
+    if (st) return st;
+    if ((int64_t)H * D > saq::kMaxRowElems) return SAQ_ERR_UNSUPPORTED;
+    const int64_t nB = ((int64_t)S + block - 1) / block;
+    if ((int64_t)B * nB >= ((int64_t)1 << 31)) return SAQ_ERR_SHAPE;
+    const size_t need = saq::select_workspace_bytes(B, H, nB, D);
+    if (!workspace || workspace_bytes < need) return SAQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return SAQ_ERR_ALIGN;
+    const size_t bytes = (size_t)B * S * H * D * 2;
+    if (overlaps(workspace, need, q_in, bytes) || overlaps(workspace, need, k_in, bytes) ||
+        overlaps(workspace, need, q_out, bytes) || overlaps(workspace, need, k_out, bytes))
+        return SAQ_ERR_ALIAS;
+    st = device_ready();
+    if (st) return st;
+    const saq::RopeTable table = make_rope_table(dt, dh, dw, rope_base);
+    return finish(saq::launch_qknorm_rope_pool(q_in, k_in, q_out, k_out, pos_thw, w_q, w_k, B, S, H, D, table,
+                                               (float)eps, block, (double*)workspace, (hipStream_t)stream));
+}
+
+int saq_select_blocks_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, double keep_ratio,
+                             uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_mask) return SAQ_ERR_NULL;
+    int st = check_dims(B, S, H, D);
+    if (st) return st;
+    st = check_block(S, block);
+    if (st) return st;
+    const int32_t nB = (S + block - 1) / block;
+    const int32_t kept = saq_kept_blocks(keep_ratio, nB);
+    if (kept < 0) return kept;
+    const size_t need = saq::select_workspace_bytes(B, H, nB, D);
+    if (!workspace || workspace_bytes < need) return SAQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return SAQ_ERR_ALIGN;
+    if (overlaps(workspace, need, block_mask, (size_t)B * H * nB * nB)) return SAQ_ERR_ALIAS;
+    st = device_ready();
+    if (st) return st;
+    return finish(saq::launch_select_from_pooled(B, S, H, D, block, kept, block_mask, workspace,
+                                                 (hipStream_t)stream));
+}
+
 int32_t saq_kept_blocks(double keep_ratio, int32_t nB) {
     if (nB < 1) return SAQ_ERR_SHAPE;
     if (!(keep_ratio > 0.0 && keep_ratio <= 1.0)) return SAQ_ERR_RANGE;

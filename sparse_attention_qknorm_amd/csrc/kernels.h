@@ -36,3 +36,21 @@ hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v,
                                     float scale, void* o, hipStream_t stream);
 
 }  // namespace saq
+
+namespace saq {
+
+// Fused prologue + pooling: also writes the per-block fp64 means of the bf16
+// q-hat and k-hat into `pooled` ([2][B][H][nB][D], the head of the selection
+// workspace). Supports H*D <= kMaxRowElems.
+constexpr int kMaxRowElems = 8192;
+
+hipError_t launch_qknorm_rope_pool(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                                   const int32_t* pos_thw, const float* w_q, const float* w_k, int32_t B,
+                                   int32_t S, int32_t H, int32_t D, const RopeTable& table, float eps,
+                                   int32_t block, double* pooled, hipStream_t stream);
+
+// Selection from pooled vectors already in the workspace (scores + top-k only).
+hipError_t launch_select_from_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, int32_t kept,
+                                     uint8_t* mask, void* workspace, hipStream_t stream);
+
+}  // namespace saq

@@ -126,3 +126,137 @@ hipError_t launch_qknorm_rope(const void* q_in, const void* k_in, void* q_out, v
 }
 
 }  // namespace saq
+
+namespace saq {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Fused form with block pooling. One workgroup per (b, block of `block` tokens,
+// group of kHeadGroup heads): 256 threads, each owning one 16-byte chunk position
+// (tensor, head, 8 channels) for the whole block. The workgroup walks the block's
+// tokens kTokStep at a time (that many loads in flight per thread), applies QKNorm
+// + RoPE as above, writes the bf16 results, and accumulates the rounded bf16 values
+// it wrote in fp64. Sums of bf16 values with |x| < 16 are exact in fp64, so the
+// means equal those of the separate pooling pass bit for bit, and the pass saves
+// that pass's re-read of q-hat and k-hat.
+template <int D>
+__global__ __launch_bounds__(kThreads) void qknorm_rope_pool_kernel(
+    const uint4* q_in, const uint4* k_in, uint4* q_out, uint4* k_out, const int32_t* __restrict__ pos_thw,
+    const float* __restrict__ w_q, const float* __restrict__ w_k, int32_t S, int32_t H, RopeTable table, float eps,
+    int32_t block, int32_t nB, int32_t n_groups, double* __restrict__ pooled) {
+    constexpr int kLanesPerRow = D / 8;
+    constexpr int kPairs = D / 2;
+    constexpr int kHeadGroup = kThreads / 2 / kLanesPerRow;   // heads per workgroup (q and k)
+    constexpr int kTokChunk = 32;                              // tokens whose angles are staged at once
+    constexpr int kTokStep = 4;                                // tokens loaded together
+    __shared__ float2 cs[kTokChunk][kPairs];
+
+    const int64_t id = blockIdx.x;                             // (b * nB + i) * n_groups + hg
+    const int hg = (int)(id % n_groups);
+    const int64_t bi = id / n_groups;
+    const int i = (int)(bi % nB);
+    const int64_t b = bi / nB;
+    const int t0 = i * block;
+    const int t1 = min(t0 + block, S);
+    const int tid = threadIdx.x;
+    const int tensor = tid / (kThreads / 2);                   // 0: q, 1: k
+    const int within = tid % (kThreads / 2);
+    const int h = hg * kHeadGroup + within / kLanesPerRow;
+    const int lane_in_row = within % kLanesPerRow;
+    const bool active = h < H;                                 // whole rows in or out together
+    const int64_t row_chunks = (int64_t)H * kLanesPerRow;      // 16-byte chunks per token per tensor
+    const uint4* src = tensor == 0 ? q_in : k_in;
+    uint4* dst = tensor == 0 ? q_out : k_out;
+    const float* wv = tensor == 0 ? w_q : w_k;
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = wv[lane_in_row * 8 + e];
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    const int64_t col = (int64_t)h * kLanesPerRow + lane_in_row;
+
+    for (int tc = t0; tc < t1; tc += kTokChunk) {
+        const int nt = min(kTokChunk, t1 - tc);
+        __syncthreads();                                       // previous chunk's angles consumed
+        for (int wi = tid; wi < nt * kPairs; wi += kThreads) {
+            const int tt = wi / kPairs, p = wi % kPairs;
+            const int axis = p < table.pair_end_t ? 0 : (p < table.pair_end_h ? 1 : 2);
+            const double theta = (double)pos_thw[(int64_t)(tc + tt) * 3 + axis] * table.inv_freq[p];
+            double sn, cn;
+            sincos(theta, &sn, &cn);
+            cs[tt][p] = make_float2((float)cn, (float)sn);
+        }
+        __syncthreads();
+        for (int ts = 0; ts < nt; ts += kTokStep) {
+            uint4 raw[kTokStep];
+#pragma unroll
+            for (int u = 0; u < kTokStep; ++u)
+                if (active && ts + u < nt) raw[u] = src[(b * S + tc + ts + u) * row_chunks + col];
+#pragma unroll
+            for (int u = 0; u < kTokStep; ++u) {
+                if (!(active && ts + u < nt)) continue;
+                const uint32_t w32[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[2 * e] = bf16_bits_to_f32(w32[e] & 0xffffu);
+                    x[2 * e + 1] = bf16_bits_to_f32(w32[e] >> 16);
+                }
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+#pragma unroll
+                for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kLanesPerRow);
+                const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+                uint32_t outw[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float2 r = cs[ts + u][lane_in_row * 4 + p];
+                    const float y0 = x[2 * p] * rinv * w[2 * p];
+                    const float y1 = x[2 * p + 1] * rinv * w[2 * p + 1];
+                    const uint32_t h0 = f32_to_bf16_bits(y0 * r.x - y1 * r.y);
+                    const uint32_t h1 = f32_to_bf16_bits(y0 * r.y + y1 * r.x);
+                    outw[p] = h0 | (h1 << 16);
+                    acc[2 * p] += (double)bf16_bits_to_f32(h0);
+                    acc[2 * p + 1] += (double)bf16_bits_to_f32(h1);
+                }
+                dst[(b * S + tc + ts + u) * row_chunks + col] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+            }
+        }
+    }
+    if (active) {
+        const int64_t Bsz = gridDim.x / ((int64_t)nB * n_groups);
+        double* out = pooled + ((((int64_t)tensor * Bsz + b) * H + h) * nB + i) * (int64_t)D + lane_in_row * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = acc[e] / (double)(t1 - t0);
+    }
+}
+
+template <int D>
+void launch_pool_d(const void* q_in, const void* k_in, void* q_out, void* k_out, const int32_t* pos_thw,
+                   const float* w_q, const float* w_k, int32_t B, int32_t S, int32_t H, const RopeTable& table,
+                   float eps, int32_t block, int32_t nB, double* pooled, hipStream_t stream) {
+    constexpr int kHeadGroup = kThreads / 2 / (D / 8);
+    const int32_t n_groups = (H + kHeadGroup - 1) / kHeadGroup;
+    hipLaunchKernelGGL((qknorm_rope_pool_kernel<D>), dim3((unsigned)((int64_t)B * nB * n_groups)), dim3(kThreads), 0,
+                       stream, (const uint4*)q_in, (const uint4*)k_in, (uint4*)q_out, (uint4*)k_out, pos_thw, w_q,
+                       w_k, S, H, table, eps, block, nB, n_groups, pooled);
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope_pool(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                                   const int32_t* pos_thw, const float* w_q, const float* w_k, int32_t B,
+                                   int32_t S, int32_t H, int32_t D, const RopeTable& table, float eps,
+                                   int32_t block, double* pooled, hipStream_t stream) {
+    const int32_t nB = (S + block - 1) / block;
+    if (D == 128)
+        launch_pool_d<128>(q_in, k_in, q_out, k_out, pos_thw, w_q, w_k, B, S, H, table, eps, block, nB, pooled, stream);
+    else
+        launch_pool_d<64>(q_in, k_in, q_out, k_out, pos_thw, w_q, w_k, B, S, H, table, eps, block, nB, pooled, stream);
+    return hipGetLastError();
+}
+
+}  // namespace saq

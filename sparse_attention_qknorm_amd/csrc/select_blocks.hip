@@ -228,26 +228,13 @@ size_t select_workspace_bytes(int64_t B, int64_t H, int64_t nB, int64_t D) {
     return ((pooled + 255) / 256) * 256 + keys;
 }
 
-hipError_t launch_select_blocks(const void* q, const void* k, int32_t B, int32_t S, int32_t H, int32_t D,
-                                int32_t block, int32_t kept, uint8_t* mask, void* workspace,
-                                hipStream_t stream) {
+hipError_t launch_select_from_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, int32_t kept,
+                                     uint8_t* mask, void* workspace, hipStream_t stream) {
     const int32_t nB = (S + block - 1) / block;
-    double* pooled = (double*)workspace;
+    const double* pq = (const double*)workspace;
+    const double* pk = pq + (size_t)B * H * nB * D;
     const size_t pooled_bytes = ((size_t)2 * B * H * nB * D * sizeof(double) + 255) / 256 * 256;
     uint64_t* keys = (uint64_t*)((char*)workspace + pooled_bytes);
-    const double* pq = pooled;
-    const double* pk = pooled + (size_t)B * H * nB * D;
-
-    const dim3 pool_grid((unsigned)((int64_t)2 * B * nB * H));
-    if (D == 128) {
-        hipLaunchKernelGGL((pool_kernel<128>), pool_grid, dim3(kThreads), 0, stream, (const uint4*)q,
-                           (const uint4*)k, pooled, S, H, block, nB);
-    } else {
-        hipLaunchKernelGGL((pool_kernel<64>), pool_grid, dim3(kThreads), 0, stream, (const uint4*)q,
-                           (const uint4*)k, pooled, S, H, block, nB);
-    }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
 
     const int32_t tiles = (nB + kTile - 1) / kTile;
     const dim3 score_grid((unsigned)((int64_t)B * H * tiles * tiles));
@@ -256,7 +243,7 @@ hipError_t launch_select_blocks(const void* q, const void* k, int32_t B, int32_t
     } else {
         hipLaunchKernelGGL((scores_kernel<64>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles);
     }
-    err = hipGetLastError();
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     const int64_t rows = (int64_t)B * H * nB;
@@ -265,6 +252,24 @@ hipError_t launch_select_blocks(const void* q, const void* k, int32_t B, int32_t
     else if (nB <= 1024) launch_topk<16>(keys, mask, nB, rows, kept, stream);
     else launch_topk<64>(keys, mask, nB, rows, kept, stream);
     return hipGetLastError();
+}
+
+hipError_t launch_select_blocks(const void* q, const void* k, int32_t B, int32_t S, int32_t H, int32_t D,
+                                int32_t block, int32_t kept, uint8_t* mask, void* workspace,
+                                hipStream_t stream) {
+    const int32_t nB = (S + block - 1) / block;
+    double* pooled = (double*)workspace;
+    const dim3 pool_grid((unsigned)((int64_t)2 * B * nB * H));
+    if (D == 128) {
+        hipLaunchKernelGGL((pool_kernel<128>), pool_grid, dim3(kThreads), 0, stream, (const uint4*)q,
+                           (const uint4*)k, pooled, S, H, block, nB);
+    } else {
+        hipLaunchKernelGGL((pool_kernel<64>), pool_grid, dim3(kThreads), 0, stream, (const uint4*)q,
+                           (const uint4*)k, pooled, S, H, block, nB);
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_select_from_pooled(B, S, H, D, block, kept, mask, workspace, stream);
 }
 
 }  // namespace saq

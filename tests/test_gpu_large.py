@@ -187,3 +187,20 @@ def test_sweep_step(step):
             _check_properties(layer, o)
             _check_attention_sample(layer, m_gpu, o, [(0, 5, 0), (0, 5, 976), (0, 5, 992), (0, 5, 500)],
                                     f"sweep step {step} keep={keep} o")
+
+
+@pytest.mark.timeout(300)
+def test_full_fused_prologue_pool_matches_separate(full):
+    # the fused prologue + pooling pass gives the same q_hat/k_hat bytes and the same mask at full size
+    c = full.cfg
+    keep = c.keep_ratios[0]
+    g = {n: full.inp[n].to(DEV) for n in ("q", "k", "pos_thw", "w_q", "w_k")}
+    qf, kf = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+    ws = saq.qknorm_rope_pool(g["q"], g["k"], qf, kf, g["pos_thw"], (g["w_q"], g["w_k"]), c.sections, c.rope_base,
+                              c.eps, c.block)
+    m_f = saq.select_blocks_pooled(qf.shape, keep, ws, c.block)
+    m_s, _ = full.run(keep)
+    torch.cuda.synchronize()
+    assert torch.equal(qf, full.qh) and torch.equal(kf, full.kh)
+    assert torch.equal(m_f, m_s)
+    log("  full: fused prologue+pooling path bit-identical (q_hat, k_hat, all 40 heads' masks)")
