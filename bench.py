@@ -128,12 +128,146 @@ def cpu_baseline(inp, cfg, keep: float, budget_s: float) -> dict:
     }
 
 
+def sweep(args) -> dict:
+    """The denoising-step sweep with gated mask reuse.
+
+    Eight steps of drifting inputs (step s = bf16(X_base + 0.05*s*Delta), composed on the device from resident
+    fp32 parts), at each keep ratio of the sweep config. Every step runs the fused prologue + pooling, then per
+    (keep, threshold) the gated selection and the attention with the mask it leaves. Measured per step: the
+    relative change of the pooled means against the previous step, the overlap of the fresh mask with the
+    previous step's fresh mask (kept blocks in both / kept blocks), the gate's decision, and when a mask is kept,
+    its overlap with the fresh mask and the output error against attention with the fresh mask."""
+    import torch
+
+    import sparse_attention_qknorm_amd as saq
+    from sparse_attention_qknorm_amd import synth
+
+    cfg = synth.get_config("sweep")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    saq.lib()
+    keeps = [args.keep] if args.keep is not None else list(cfg.keep_ratios)
+    thresholds = [float(x) for x in args.reuse_thresholds.split(",")]
+    log(f"[sweep] generating base and drift tensors (S={cfg.S} H={cfg.H} D={cfg.D})")
+    t0 = time.perf_counter()
+    parts = {}
+    for n in ("q", "k", "v"):
+        b, d = synth.sweep_parts(cfg, n)
+        parts[n] = (b.to(dev), d.to(dev))
+        del b, d
+        log(f"[sweep] {n} ready ({time.perf_counter() - t0:.0f} s)")
+    common = synth.make_inputs(cfg, tensors=())
+    pos, wq, wk = common["pos_thw"].to(dev), common["w_q"].to(dev), common["w_k"].to(dev)
+    shape = (cfg.B, cfg.S, cfg.H, cfg.D)
+    x = {n: torch.empty(shape, dtype=torch.bfloat16, device=dev) for n in ("q", "k", "v")}
+    qh, kh = torch.empty_like(x["q"]), torch.empty_like(x["k"])
+    wsb = saq.select_workspace_bytes(*shape, cfg.block)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(2)]
+    o_used, o_fresh = torch.empty_like(qh), torch.empty_like(qh)
+    fresh = {kp: torch.empty((cfg.B, cfg.H, cfg.nB, cfg.nB), dtype=torch.uint8, device=dev) for kp in keeps}
+    prev_fresh = {kp: torch.empty_like(fresh[kp]) for kp in keeps}
+    reuse = {(kp, t): saq.MaskReuse(shape, kp, t, cfg.block, dev) for kp in keeps for t in thresholds}
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        return a, b
+
+    rows = []
+    for step in range(cfg.steps):
+        for n in ("q", "k", "v"):
+            synth.compose_sweep_step(*parts[n], cfg.drift, step, out=x[n])
+        cur, prev = ws[step % 2], ws[(step + 1) % 2]
+        ev_pro = timed(lambda: saq.qknorm_rope_pool(x["q"], x["k"], qh, kh, pos, (wq, wk), cfg.sections,
+                                                     cfg.rope_base, cfg.eps, cfg.block, workspace=cur))
+        change = saq.pooled_change(prev, cur, shape, cfg.block) if step else None
+        row = {"step": step, "per_keep": {}}
+        pending = []
+        for kp in keeps:
+            ev_fresh = timed(lambda: saq.select_blocks_pooled(shape, kp, cur, cfg.block, out=fresh[kp]))
+            ent = {"fresh_select": ev_fresh, "thr": {}}
+            if step:
+                ent["overlap_prev"] = saq.mask_overlap(fresh[kp], prev_fresh[kp])
+            for t in thresholds:
+                r = reuse[(kp, t)]
+                ev_sel = timed(lambda: r.step(cur))
+                ev_att = timed(lambda: saq.block_sparse_attn(qh, kh, x["v"], r.mask, cfg.block, out=o_used))
+                te = {"sel": ev_sel, "att": ev_att, "ov_fresh": saq.mask_overlap(r.mask, fresh[kp])}
+                torch.cuda.synchronize()
+                if not r.recomputed():
+                    saq.block_sparse_attn(qh, kh, x["v"], fresh[kp], cfg.block, out=o_fresh)
+                    diff = (o_used.float() - o_fresh.float())
+                    te["err"] = (float(diff.abs().max().item()),
+                                 float(diff.norm().item() / max(o_fresh.float().norm().item(), 1e-30)))
+                te["recomputed"] = r.recomputed()
+                te["change_vs_ref"] = r.relative_change() if step else None
+                ent["thr"][t] = te
+            prev_fresh[kp].copy_(fresh[kp])
+            row["per_keep"][kp] = ent
+        torch.cuda.synchronize()
+        row["pro_ms"] = ev_pro[0].elapsed_time(ev_pro[1])
+        if change is not None:
+            d2, p2 = change[:2].tolist()
+            row["change_prev"] = (d2 / p2) ** 0.5
+        line = [f"step {step}: prologue+pool {row['pro_ms']:.2f} ms"]
+        if step:
+            line.append(f"pooled change vs prev {row['change_prev']:.5f}")
+        for kp, ent in row["per_keep"].items():
+            ent["fresh_ms"] = ent.pop("fresh_select")
+            ent["fresh_ms"] = ent["fresh_ms"][0].elapsed_time(ent["fresh_ms"][1])
+            if "overlap_prev" in ent:
+                c = ent["overlap_prev"].sum(dim=(0, 1)).tolist()
+                ent["overlap_prev"] = c[0] / c[1]
+            for t, te in ent["thr"].items():
+                te["sel_ms"] = te.pop("sel")
+                te["sel_ms"] = te["sel_ms"][0].elapsed_time(te["sel_ms"][1])
+                te["att_ms"] = te.pop("att")
+                te["att_ms"] = te["att_ms"][0].elapsed_time(te["att_ms"][1])
+                c = te.pop("ov_fresh").sum(dim=(0, 1)).tolist()
+                te["overlap_with_fresh"] = c[0] / c[1]
+            line.append(f"keep {kp}: overlap vs prev {ent.get('overlap_prev', 1.0):.4f}, decisions " +
+                        " ".join(f"{t}:{'R' if te['recomputed'] else 'K'}" for t, te in ent["thr"].items()))
+        log("[sweep] " + "; ".join(line))
+        rows.append(row)
+
+    # summary per (keep, threshold): recompute count, worst output error of a kept mask, time saved
+    summary = {}
+    for kp in keeps:
+        for t in thresholds:
+            tes = [r["per_keep"][kp]["thr"][t] for r in rows]
+            kept = [te for te in tes if not te["recomputed"]]
+            fresh_ms = sum(r["per_keep"][kp]["fresh_ms"] for r in rows)
+            gated_ms = sum(te["sel_ms"] for te in tes)
+            summary[f"keep={kp},threshold={t}"] = {
+                "recomputed_steps": [r["step"] for r, te in zip(rows, tes) if te["recomputed"]],
+                "kept_mask_overlap_with_fresh_min": min([te["overlap_with_fresh"] for te in kept], default=1.0),
+                "kept_mask_o_max_abs_vs_fresh": max([te["err"][0] for te in kept], default=0.0),
+                "kept_mask_o_rel_fro_vs_fresh": max([te["err"][1] for te in kept], default=0.0),
+                "select_ms_total_always": fresh_ms,
+                "select_ms_total_gated": gated_ms,
+                "attn_ms_total": sum(te["att_ms"] for te in tes),
+            }
+    per_step = [{"step": r["step"], "prologue_pool_ms": r["pro_ms"], "pooled_change_vs_prev": r.get("change_prev"),
+                 "mask_overlap_vs_prev": {str(kp): r["per_keep"][kp].get("overlap_prev") for kp in keeps},
+                 "fresh_select_ms": {str(kp): r["per_keep"][kp]["fresh_ms"] for kp in keeps}} for r in rows]
+    return {"workload": f"sweep: {cfg.steps} denoising steps of the full layer (S={cfg.S}, H={cfg.H}, D={cfg.D}), "
+                        f"step s = bf16(X_base + {cfg.drift}*s*Delta)",
+            "keeps": keeps, "thresholds": thresholds, "per_step": per_step, "summary": summary}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="full", choices=["full", "medium", "small", "tiny"])
+    ap.add_argument("--workload", default="full", choices=["full", "medium", "small", "tiny", "sweep"],
+                    help="sweep: the 8-step drift sweep with gated mask reuse (a measurement of the reuse gate, "
+                         "printed as its own JSON line)")
+    ap.add_argument("--reuse-thresholds", default="0.005,0.01,0.02,0.04",
+                    help="sweep only: relative pooled-change thresholds of the mask-reuse gate")
     ap.add_argument("--keep", type=float, default=None, help="keep ratio (default: the config's first)")
     ap.add_argument("--path", default="fused", choices=["fused", "split"],
                     help="fused: prologue with block pooling folded in, then selection from the pooled vectors; "
@@ -149,6 +283,11 @@ def main(argv=None) -> int:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer would shard by "
               "heads; see the design notes). Run with --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.workload == "sweep":
+        print(json.dumps({"metric": "mask reuse across denoising steps (gate decisions, overlap, output error)",
+                          "n_gpus": 1, "data": "synthetic", **sweep(args)}), flush=True)
+        return 0
 
     import torch
 

@@ -171,6 +171,63 @@ int saq_qknorm_rope_pool(const void* q_in, const void* k_in, void* q_out, void* 
 int saq_select_blocks_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, double keep_ratio,
                              uint8_t* block_mask, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Cross-step mask reuse, measured (Sol Engine "H3 on device" page, cross-step
+ * cache paragraph: consecutive denoising steps are nearly identical through the
+ * middle of the schedule, and a cheap change detector decides what to recompute).
+ *
+ * saq_mask_overlap: for two masks [B,H,nB,nB] (non-zero byte = kept), writes
+ * counts[2*(b*H+h)] = #(kept in both), counts[2*(b*H+h)+1] = #(kept in a).
+ * counts: device int64 [2*B*H]. Exact integers.
+ *
+ * saq_pooled_change: the change detector on the pooled block means that
+ * saq_qknorm_rope_pool leaves in a selection workspace. With P = all 2*B*H*nB*D
+ * pooled values, writes out[0] = sum (P_cur - P_prev)^2 and
+ * out[1] = sum P_prev^2 in fp64 (fixed reduction order: identical bits on every
+ * run); the relative change is sqrt(out[0] / out[1]). out: device double array
+ * of at least saq_pooled_change_out_len() entries (the rest is scratch).
+ */
+int saq_mask_overlap(const uint8_t* mask_a, const uint8_t* mask_b, int32_t B, int32_t H, int32_t nB,
+                     int64_t* counts, void* stream);
+size_t saq_pooled_change_out_len(void);
+int saq_pooled_change(const void* workspace_prev, const void* workspace_cur, int32_t B, int32_t S, int32_t H,
+                      int32_t D, int32_t block, double* out, size_t out_len, void* stream);
+
+/*
+ * Gated block selection for a step loop: the mask of an earlier step is kept
+ * while the pooled block means it was selected from have barely moved, in the
+ * manner of the cross-step cache on the same page (one threshold on a cheap
+ * relative-change signal). The decision is taken on the device, so the call
+ * needs no host round trip and the stream stays asynchronous.
+ *
+ * Inputs: `workspace` as left by saq_qknorm_rope_pool for the current step
+ * (the current pooled means P_cur); `pooled_ref`, a caller-owned device buffer
+ * of saq_pooled_bytes(...) bytes (16-byte aligned) holding the pooled means P_ref
+ * the mask in `block_mask` was selected from; `state`, a device double array of
+ * saq_reuse_state_len() entries (8-byte aligned).
+ *
+ * Steps, in stream order:
+ *   1. state[0] = sum (P_cur - P_ref)^2, state[1] = sum P_ref^2 (fp64, fixed
+ *      reduction order, as saq_pooled_change);
+ *   2. the mask is kept iff force == 0 and state[0] <= (threshold*threshold) *
+ *      state[1] (fp64, evaluated in that order); state[2] = 0.0 if kept,
+ *      1.0 if recomputed;
+ *   3. if recomputed: block_mask = saq_select_blocks_pooled(...) on `workspace`
+ *      (bit-identical), then pooled_ref = P_cur; if kept, block_mask and
+ *      pooled_ref are left untouched.
+ * The rest of `state` is scratch. On the first step of a loop pass force = 1
+ * (pooled_ref may then hold anything finite, or anything at all: it only feeds
+ * state[0..1]). threshold: finite and >= 0 (SAQ_ERR_RANGE otherwise); 0 keeps
+ * the mask only when the pooled means are unchanged. No buffer may overlap
+ * another (SAQ_ERR_ALIAS).
+ */
+size_t saq_pooled_bytes(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block);
+size_t saq_reuse_state_len(void);
+int saq_select_blocks_reuse(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, double keep_ratio,
+                            double threshold, int32_t force, uint8_t* block_mask, void* workspace,
+                            size_t workspace_bytes, void* pooled_ref, size_t pooled_ref_bytes, double* state,
+                            size_t state_len, void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* saq_status_string(int status);
 

@@ -27,6 +27,10 @@ What it computes, in the order of the layer:
    Sol-H3, "Specific outcomes of key optimizations"); the rule is the build's.
 4. Block-sparse attention (``block_sparse_attention``): non-causal softmax
    attention of each query block over the tokens of its kept key blocks only.
+5. Cross-step reuse measurements (``mask_overlap``, ``pooled_change``): the
+   overlap of two steps' masks and the relative change of their pooled block
+   means, the detector that gates reusing a mask (cross-step cache paragraph of
+   the "H3 on device" page).
 
 Every function is pinned by CPU tests to something other than itself: closed
 forms, invariants, library routines (complex multiplication, logspace,
@@ -40,9 +44,11 @@ from .prologue import qknorm, rope_inv_freq, rope_3d, qknorm_rope
 from .selection import (num_kept_blocks, pool_blocks, block_scores, select_topk,
                         select_blocks, block_token_range)
 from .attention import block_sparse_attention, block_sparse_attention_rows, dense_attention
+from .step_reuse import mask_overlap, pooled_change, relative_change, keeps_mask, reuse_schedule
 
 __all__ = [
     "qknorm", "rope_inv_freq", "rope_3d", "qknorm_rope",
     "num_kept_blocks", "pool_blocks", "block_scores", "select_topk", "select_blocks",
     "block_token_range", "block_sparse_attention", "block_sparse_attention_rows", "dense_attention",
+    "mask_overlap", "pooled_change", "relative_change", "keeps_mask", "reuse_schedule",
 ]

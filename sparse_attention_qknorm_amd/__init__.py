@@ -22,7 +22,8 @@ import torch
 from ._binding import SaqError, check, lib
 
 __all__ = ["qknorm_rope", "qknorm_rope_out", "qknorm_rope_pool", "select_blocks", "select_blocks_pooled",
-           "select_workspace_bytes", "block_sparse_attn", "kept_blocks", "SaqError", "lib"]
+           "select_workspace_bytes", "block_sparse_attn", "kept_blocks", "mask_overlap", "pooled_change", "pooled_bytes",
+           "MaskReuse", "SaqError", "lib"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -168,3 +169,75 @@ def block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_m
                                      block, float(softmax_scale), out.data_ptr(), _stream(q))
     check(st, "saq_block_sparse_attn")
     return out
+
+
+def mask_overlap(mask_a: torch.Tensor, mask_b: torch.Tensor) -> torch.Tensor:
+    """int64 [B, H, 2]: (#kept in both masks, #kept in mask_a) per head (saq_mask_overlap)."""
+    for n, m in (("mask_a", mask_a), ("mask_b", mask_b)):
+        if m.dtype != torch.uint8 or m.dim() != 4 or not m.is_contiguous() or not m.is_cuda:
+            raise ValueError(f"{n} must be a contiguous uint8 [B,H,nB,nB] device tensor")
+    if mask_a.shape != mask_b.shape:
+        raise ValueError("masks must have the same shape")
+    B, H, nB, _ = mask_a.shape
+    counts = torch.empty((B, H, 2), dtype=torch.int64, device=mask_a.device)
+    st = lib().saq_mask_overlap(mask_a.data_ptr(), mask_b.data_ptr(), B, H, nB, counts.data_ptr(), _stream(mask_a))
+    check(st, "saq_mask_overlap")
+    return counts
+
+
+def pooled_change(ws_prev: torch.Tensor, ws_cur: torch.Tensor, shape: Sequence[int], block: int = 128,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp64 device tensor whose [0] = sum (P_cur - P_prev)^2 and [1] = sum P_prev^2 over the pooled block means
+    in two selection workspaces (saq_pooled_change). The relative change is sqrt([0] / [1])."""
+    B, S, H, D = (int(x) for x in shape)
+    n = lib().saq_pooled_change_out_len()
+    if out is None:
+        out = torch.empty(n, dtype=torch.float64, device=ws_cur.device)
+    st = lib().saq_pooled_change(ws_prev.data_ptr(), ws_cur.data_ptr(), B, S, H, D, block, out.data_ptr(),
+                                 out.numel(), _stream(ws_cur))
+    check(st, "saq_pooled_change")
+    return out
+
+
+def pooled_bytes(B: int, S: int, H: int, D: int, block: int = 128) -> int:
+    """Bytes of the pooled fp64 block means of q and k, [2][B][H][nB][D] (saq_pooled_bytes)."""
+    n = lib().saq_pooled_bytes(B, S, H, D, block)
+    if n == 0:
+        raise ValueError(f"unsupported shape B={B} S={S} H={H} D={D} block={block}")
+    return n
+
+
+class MaskReuse:
+    """Device buffers of one gated-selection loop (saq_select_blocks_reuse): the mask in use, the pooled means it
+    was selected from, and the decision state. `step` keeps or recomputes the mask on the device, without a host
+    round trip; `recomputed()` and `relative_change()` read the last decision back (they synchronise)."""
+
+    def __init__(self, shape: Sequence[int], keep_ratio: float, threshold: float, block: int = 128,
+                 device="cuda:0"):
+        self.shape = tuple(int(x) for x in shape)
+        B, S, H, D = self.shape
+        nB = -(-S // block)
+        self.keep_ratio, self.threshold, self.block = float(keep_ratio), float(threshold), int(block)
+        self.mask = torch.zeros((B, H, nB, nB), dtype=torch.uint8, device=device)
+        self.pooled_ref = torch.zeros(pooled_bytes(B, S, H, D, block), dtype=torch.uint8, device=device)
+        self.state = torch.zeros(lib().saq_reuse_state_len(), dtype=torch.float64, device=device)
+        self.started = False
+
+    def step(self, workspace: torch.Tensor, force: bool = False) -> torch.Tensor:
+        B, S, H, D = self.shape
+        f = 1 if (force or not self.started) else 0
+        st = lib().saq_select_blocks_reuse(B, S, H, D, self.block, self.keep_ratio, self.threshold, f,
+                                           self.mask.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), self.pooled_ref.data_ptr(),
+                                           self.pooled_ref.numel(), self.state.data_ptr(), self.state.numel(),
+                                           _stream(workspace))
+        check(st, "saq_select_blocks_reuse")
+        self.started = True
+        return self.mask
+
+    def recomputed(self) -> bool:
+        return bool(self.state[2].item() != 0.0)
+
+    def relative_change(self) -> float:
+        d2, p2 = self.state[:2].tolist()
+        return (d2 / p2) ** 0.5 if p2 > 0 else (0.0 if d2 == 0 else float("inf"))

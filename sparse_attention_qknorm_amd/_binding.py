@@ -37,6 +37,13 @@ SIGNATURES = [
     ("saq_qknorm_rope_pool", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f64, _f64, _i32, _vp, _sz, _vp]),
     ("saq_select_blocks_pooled", ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp, _sz, _vp]),
+    ("saq_mask_overlap", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    ("saq_pooled_change_out_len", _sz, []),
+    ("saq_pooled_change", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    ("saq_pooled_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
+    ("saq_reuse_state_len", _sz, []),
+    ("saq_select_blocks_reuse", ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _f64, _f64, _i32, _vp, _vp, _sz, _vp,
+                                               _sz, _vp, _sz, _vp]),
     ("saq_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("saq_last_hip_error", ctypes.c_int, []),
 ]

@@ -151,6 +151,80 @@ int saq_select_blocks_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t
                                                  (hipStream_t)stream));
 }
 
+int saq_mask_overlap(const uint8_t* mask_a, const uint8_t* mask_b, int32_t B, int32_t H, int32_t nB,
+                     int64_t* counts, void* stream) {
+    if (!mask_a || !mask_b || !counts) return SAQ_ERR_NULL;
+    if (B < 1 || H < 1 || nB < 1 || nB > saq::kMaxBlocks) return SAQ_ERR_SHAPE;
+    if (((uintptr_t)counts & 7u) != 0) return SAQ_ERR_ALIGN;
+    const size_t mbytes = (size_t)B * H * nB * nB;
+    if (overlaps(counts, (size_t)B * H * 16, mask_a, mbytes) || overlaps(counts, (size_t)B * H * 16, mask_b, mbytes))
+        return SAQ_ERR_ALIAS;
+    const int st = device_ready();
+    if (st) return st;
+    return finish(saq::launch_mask_overlap(mask_a, mask_b, B, H, nB, counts, (hipStream_t)stream));
+}
+
+size_t saq_pooled_change_out_len(void) { return 2 + 2 * (size_t)saq::kChangeGroups; }
+
+int saq_pooled_change(const void* workspace_prev, const void* workspace_cur, int32_t B, int32_t S, int32_t H,
+                      int32_t D, int32_t block, double* out, size_t out_len, void* stream) {
+    if (!workspace_prev || !workspace_cur || !out) return SAQ_ERR_NULL;
+    int st = check_dims(B, S, H, D);
+    if (st) return st;
+    st = check_block(S, block);
+    if (st) return st;
+    if (out_len < saq_pooled_change_out_len()) return SAQ_ERR_WORKSPACE;
+    if (((uintptr_t)out & 7u) != 0 || ((uintptr_t)workspace_prev & 255u) != 0 || ((uintptr_t)workspace_cur & 255u) != 0)
+        return SAQ_ERR_ALIGN;
+    const int64_t nB = ((int64_t)S + block - 1) / block;
+    const int64_t n = 2 * (int64_t)B * H * nB * D;
+    if (overlaps(out, out_len * 8, workspace_prev, (size_t)n * 8) || overlaps(out, out_len * 8, workspace_cur, (size_t)n * 8))
+        return SAQ_ERR_ALIAS;
+    st = device_ready();
+    if (st) return st;
+    return finish(saq::launch_pooled_change((const double*)workspace_prev, (const double*)workspace_cur, n, out,
+                                            (hipStream_t)stream));
+}
+
+size_t saq_pooled_bytes(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block) {
+    if (check_dims(B, S, H, D) || check_block(S, block)) return 0;
+    const int64_t nB = ((int64_t)S + block - 1) / block;
+    return (size_t)2 * B * H * nB * D * sizeof(double);
+}
+
+size_t saq_reuse_state_len(void) { return (size_t)saq::kReuseStateLen; }
+
+int saq_select_blocks_reuse(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, double keep_ratio,
+                            double threshold, int32_t force, uint8_t* block_mask, void* workspace,
+                            size_t workspace_bytes, void* pooled_ref, size_t pooled_ref_bytes, double* state,
+                            size_t state_len, void* stream) {
+    if (!block_mask || !workspace || !pooled_ref || !state) return SAQ_ERR_NULL;
+    int st = check_dims(B, S, H, D);
+    if (st) return st;
+    st = check_block(S, block);
+    if (st) return st;
+    const int32_t nB = (S + block - 1) / block;
+    const int32_t kept = saq_kept_blocks(keep_ratio, nB);
+    if (kept < 0) return kept;
+    if (!(threshold >= 0.0) || !isfinite(threshold)) return SAQ_ERR_RANGE;
+    const size_t need = saq::select_workspace_bytes(B, H, nB, D);
+    const size_t pooled = saq_pooled_bytes(B, S, H, D, block);
+    if (workspace_bytes < need || pooled_ref_bytes < pooled || state_len < saq_reuse_state_len())
+        return SAQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0 || ((uintptr_t)pooled_ref & 15u) != 0 || ((uintptr_t)state & 7u) != 0)
+        return SAQ_ERR_ALIGN;
+    const size_t mbytes = (size_t)B * H * nB * nB;
+    const size_t sbytes = state_len * sizeof(double);
+    if (overlaps(workspace, need, block_mask, mbytes) || overlaps(pooled_ref, pooled, workspace, need) ||
+        overlaps(pooled_ref, pooled, block_mask, mbytes) || overlaps(state, sbytes, workspace, need) ||
+        overlaps(state, sbytes, pooled_ref, pooled) || overlaps(state, sbytes, block_mask, mbytes))
+        return SAQ_ERR_ALIAS;
+    st = device_ready();
+    if (st) return st;
+    return finish(saq::launch_select_reuse(B, S, H, D, block, kept, workspace, (double*)pooled_ref, threshold,
+                                           force != 0 ? 1 : 0, block_mask, state, (hipStream_t)stream));
+}
+
 int32_t saq_kept_blocks(double keep_ratio, int32_t nB) {
     if (nB < 1) return SAQ_ERR_SHAPE;
     if (!(keep_ratio > 0.0 && keep_ratio <= 1.0)) return SAQ_ERR_RANGE;

@@ -50,7 +50,31 @@ hipError_t launch_qknorm_rope_pool(const void* q_in, const void* k_in, void* q_o
                                    int32_t block, double* pooled, hipStream_t stream);
 
 // Selection from pooled vectors already in the workspace (scores + top-k only).
+// With a gate, both kernels read *gate on the device and do nothing when it is 0.0.
 hipError_t launch_select_from_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, int32_t kept,
-                                     uint8_t* mask, void* workspace, hipStream_t stream);
+                                     uint8_t* mask, void* workspace, hipStream_t stream,
+                                     const double* gate = nullptr);
+
+}  // namespace saq
+
+namespace saq {
+
+// Cross-step reuse measurements (step_reuse.hip).
+constexpr int kChangeGroups = 512;   // workgroups of the first pooled-change stage
+
+hipError_t launch_mask_overlap(const uint8_t* a, const uint8_t* b, int32_t B, int32_t H, int32_t nB, int64_t* counts,
+                               hipStream_t stream);
+
+// out: [2 + 2*kChangeGroups] doubles; out[0] = sum (cur-prev)^2, out[1] = sum prev^2
+hipError_t launch_pooled_change(const double* prev, const double* cur, int64_t n, double* out, hipStream_t stream);
+
+// Gated selection. state: [kReuseStateLen] doubles; state[0..1] as out[0..1] of
+// launch_pooled_change between ref and cur, state[2] = 1.0 if the mask is
+// recomputed, 0.0 if the previous one is kept; the rest is scratch. On
+// recompute, cur's pooled vectors are also copied into ref.
+constexpr int kReuseStateLen = 4 + 2 * kChangeGroups;
+hipError_t launch_select_reuse(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, int32_t kept,
+                               void* workspace_cur, double* pooled_ref, double threshold, int32_t force,
+                               uint8_t* mask, double* state, hipStream_t stream);
 
 }  // namespace saq

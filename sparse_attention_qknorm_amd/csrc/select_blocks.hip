@@ -97,10 +97,12 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void scores_kernel(const double* __restrict__ pq, const double* __restrict__ pk,
-                                                          uint64_t* __restrict__ keys, int32_t nB, int32_t tiles) {
+                                                          uint64_t* __restrict__ keys, int32_t nB, int32_t tiles,
+                                                          const double* __restrict__ gate) {
 #pragma clang fp contract(off)
     __shared__ double sq[kSlice][kTile];
     __shared__ double sk[kSlice][kTile];
+    if (gate != nullptr && *gate == 0.0) return;        // the mask of an earlier step is kept
 
     const int64_t bh = blockIdx.x / ((int64_t)tiles * tiles);
     const int tile = (int)(blockIdx.x % ((int64_t)tiles * tiles));
@@ -166,7 +168,9 @@ __device__ __forceinline__ int wave_count(bool p) {
 
 template <int R>   // keys per lane: nB <= 64 * R
 __global__ __launch_bounds__(kThreads) void topk_kernel(const uint64_t* __restrict__ keys, uint8_t* __restrict__ mask,
-                                                        int32_t nB, int64_t rows, int32_t kept) {
+                                                        int32_t nB, int64_t rows, int32_t kept,
+                                                        const double* __restrict__ gate) {
+    if (gate != nullptr && *gate == 0.0) return;
     const int lane = threadIdx.x % kWave;
     const int64_t row = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
     if (row >= rows) return;                              // whole wave leaves together
@@ -214,10 +218,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const uint64_t* __restri
 }
 
 template <int R>
-void launch_topk(const uint64_t* keys, uint8_t* mask, int32_t nB, int64_t rows, int32_t kept, hipStream_t stream) {
+void launch_topk(const uint64_t* keys, uint8_t* mask, int32_t nB, int64_t rows, int32_t kept, const double* gate,
+                 hipStream_t stream) {
     const int64_t waves_per_wg = kThreads / kWave;
     const dim3 grid((unsigned)((rows + waves_per_wg - 1) / waves_per_wg));
-    hipLaunchKernelGGL((topk_kernel<R>), grid, dim3(kThreads), 0, stream, keys, mask, nB, rows, kept);
+    hipLaunchKernelGGL((topk_kernel<R>), grid, dim3(kThreads), 0, stream, keys, mask, nB, rows, kept, gate);
 }
 
 }  // namespace
@@ -229,7 +234,7 @@ size_t select_workspace_bytes(int64_t B, int64_t H, int64_t nB, int64_t D) {
 }
 
 hipError_t launch_select_from_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, int32_t kept,
-                                     uint8_t* mask, void* workspace, hipStream_t stream) {
+                                     uint8_t* mask, void* workspace, hipStream_t stream, const double* gate) {
     const int32_t nB = (S + block - 1) / block;
     const double* pq = (const double*)workspace;
     const double* pk = pq + (size_t)B * H * nB * D;
@@ -239,18 +244,20 @@ hipError_t launch_select_from_pooled(int32_t B, int32_t S, int32_t H, int32_t D,
     const int32_t tiles = (nB + kTile - 1) / kTile;
     const dim3 score_grid((unsigned)((int64_t)B * H * tiles * tiles));
     if (D == 128) {
-        hipLaunchKernelGGL((scores_kernel<128>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles);
+        hipLaunchKernelGGL((scores_kernel<128>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles,
+                           gate);
     } else {
-        hipLaunchKernelGGL((scores_kernel<64>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles);
+        hipLaunchKernelGGL((scores_kernel<64>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles,
+                           gate);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     const int64_t rows = (int64_t)B * H * nB;
-    if (nB <= 64) launch_topk<1>(keys, mask, nB, rows, kept, stream);
-    else if (nB <= 256) launch_topk<4>(keys, mask, nB, rows, kept, stream);
-    else if (nB <= 1024) launch_topk<16>(keys, mask, nB, rows, kept, stream);
-    else launch_topk<64>(keys, mask, nB, rows, kept, stream);
+    if (nB <= 64) launch_topk<1>(keys, mask, nB, rows, kept, gate, stream);
+    else if (nB <= 256) launch_topk<4>(keys, mask, nB, rows, kept, gate, stream);
+    else if (nB <= 1024) launch_topk<16>(keys, mask, nB, rows, kept, gate, stream);
+    else launch_topk<64>(keys, mask, nB, rows, kept, gate, stream);
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ import torch
 
 __all__ = [
     "LayerConfig", "CONFIGS", "get_config", "positions_thw", "make_inputs",
-    "make_sweep_inputs", "rng_for", "bf16_from_f32",
+    "make_sweep_inputs", "sweep_parts", "compose_sweep_step", "rng_for", "bf16_from_f32",
 ]
 
 
@@ -216,6 +216,30 @@ def make_sweep_inputs(cfg: LayerConfig | str, step: int, tensors: Sequence[str] 
         del x
     out["pos_thw"] = torch.from_numpy(positions_thw(cfg.T, cfg.Hg, cfg.W, cfg.A))
     out["w_q"], out["w_k"] = _weights(cfg)
+    return out
+
+
+def sweep_parts(cfg: LayerConfig | str, name: str):
+    """(X_base, Delta) of tensor `name` of the sweep as fp32 torch tensors [B, S, H, D] on the host, so that a
+    step can be composed where the data lives (``compose_sweep_step``)."""
+    if isinstance(cfg, str):
+        cfg = get_config(cfg)
+    which = ("q", "k", "v").index(name)
+    u_qk, u_v, phi = _dirs(cfg)
+    x = _base_f32(cfg, which, u_v if name == "v" else u_qk, phi)
+    delta = _noise(SWEEP_DRIFT_INDEX, which, x.shape)
+    return torch.from_numpy(x), torch.from_numpy(delta)
+
+
+def compose_sweep_step(base: torch.Tensor, delta: torch.Tensor, drift: float, step: int,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16(base + fp32(drift*step) * delta) with the product and the sum each rounded to fp32 (two separate
+    elementwise ops, as make_sweep_inputs does on the host), on whatever device the tensors are on."""
+    c = torch.tensor(np.float32(drift * step), dtype=torch.float32, device=base.device)
+    x = base if step == 0 else base + delta * c
+    if out is None:
+        return x.to(torch.bfloat16)
+    out.copy_(x)
     return out
 
 

@@ -140,3 +140,58 @@ def test_valid_call_without_device_reports_no_device():
     lib = _binding.lib()
     st = lib.saq_block_sparse_attn(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 1, 1024, 2, 64, 64, 0.0, 1 << 24, None)
     assert st == -8
+
+
+def test_step_reuse_validation():
+    lib = _binding.lib()
+    # S=1024, H=2, D=64, block=64: nB=16, pooled 32 KiB, workspace 36 KiB
+    assert lib.saq_pooled_bytes(1, 1024, 2, 64, 64) == 2 * 2 * 16 * 64 * 8
+    assert lib.saq_pooled_bytes(1, 1024, 2, 96, 64) == 0
+    n_state = lib.saq_reuse_state_len()
+    assert n_state >= 3
+
+    def call(mask=FAKE * 3, ws=1 << 24, wbytes=1 << 20, ref=1 << 25, rbytes=1 << 20, state=1 << 26, slen=n_state,
+             keep=0.5, thr=0.05, S=1024, block=64):
+        return lib.saq_select_blocks_reuse(1, S, 2, 64, block, keep, thr, 0, mask, ws, wbytes, ref, rbytes, state,
+                                           slen, None)
+
+    assert call(mask=None) == -1 and call(ref=None) == -1 and call(state=None) == -1
+    assert call(block=32) == -3
+    assert call(keep=0.0) == -5 and call(thr=-1e-3) == -5 and call(thr=float("nan")) == -5
+    assert call(thr=float("inf")) == -5
+    assert call(wbytes=100) == -6 and call(rbytes=32767) == -6 and call(slen=n_state - 1) == -6
+    assert call(ws=(1 << 24) + 16) == -4 and call(ref=(1 << 25) + 8) == -4 and call(state=(1 << 26) + 4) == -4
+    assert call(ref=(1 << 24) + 4096) == -9            # reference inside the workspace
+    assert call(state=(1 << 25) + 256) == -9           # state inside the reference
+
+    # pooled change / overlap
+    out_len = lib.saq_pooled_change_out_len()
+    assert lib.saq_pooled_change(None, 1 << 24, 1, 1024, 2, 64, 64, 1 << 26, out_len, None) == -1
+    assert lib.saq_pooled_change(1 << 25, 1 << 24, 1, 1024, 2, 64, 64, 1 << 26, out_len - 1, None) == -6
+    assert lib.saq_pooled_change(1 << 25, 1 << 24, 1, 1024, 2, 64, 64, (1 << 24) + 64, out_len, None) == -9
+    assert lib.saq_mask_overlap(FAKE, None, 1, 2, 16, 1 << 24, None) == -1
+    assert lib.saq_mask_overlap(FAKE, FAKE * 2, 1, 2, 0, 1 << 24, None) == -2
+    assert lib.saq_mask_overlap(FAKE, FAKE * 2, 1, 2, 16, (1 << 24) + 4, None) == -4
+
+
+def test_fused_prologue_pool_validation():
+    lib = _binding.lib()
+
+    def pool(q=FAKE, k=FAKE * 2, qo=FAKE * 3, ko=FAKE * 4, H=2, D=64, block=64, ws=1 << 24, wbytes=1 << 20):
+        sec = (16, 24, 24) if D == 64 else (32, 48, 48)
+        return lib.saq_qknorm_rope_pool(q, k, qo, ko, FAKE * 5, FAKE * 6, FAKE * 7, 1, 16, H, D, *sec, 1e4,
+                                        1e-6, block, ws, wbytes, None)
+
+    assert pool(q=None) == -1
+    far = dict(q=1 << 27, k=2 << 27, qo=3 << 27, ko=4 << 27)
+    assert pool(H=64, D=128, **far, wbytes=8) == -6                   # H*D = 8192 passes that check
+    assert pool(H=65, D=128, **far, wbytes=8) == -3                   # H*D > 8192
+    assert pool(block=96) == -3
+    assert pool(wbytes=8) == -6
+    assert pool(ws=(1 << 24) + 128) == -4
+
+    def sel(mask=FAKE, ws=1 << 24, wbytes=1 << 20, keep=0.5):
+        return lib.saq_select_blocks_pooled(1, 1024, 2, 64, 64, keep, mask, ws, wbytes, None)
+
+    assert sel(mask=None) == -1 and sel(keep=2.0) == -5 and sel(wbytes=0) == -6
+    assert sel(mask=(1 << 24) + 64) == -9

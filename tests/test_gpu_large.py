@@ -204,3 +204,45 @@ def test_full_fused_prologue_pool_matches_separate(full):
     assert torch.equal(qf, full.qh) and torch.equal(kf, full.kh)
     assert torch.equal(m_f, m_s)
     log("  full: fused prologue+pooling path bit-identical (q_hat, k_hat, all 40 heads' masks)")
+
+
+@pytest.mark.timeout(400)
+def test_full_sweep_reuse(full):
+    # sweep step 1 against step 0 (the full inputs) at the full size: the pooled-change sums
+    # against the oracle's exactly rounded sums of the same pooled means, the overlap counts
+    # of the two fresh masks bit-exact, and the gate on either side of the measured change
+    c = full.cfg
+    keep = c.keep_ratios[0]
+    cfg_s = synth.get_config("sweep")
+    log("[full] generating sweep step 1 (q, k)")
+    s1 = synth.make_sweep_inputs(cfg_s, 1, tensors=("q", "k"))
+    pos, wq, wk = (full.inp[n].to(DEV) for n in ("pos_thw", "w_q", "w_k"))
+    ws, masks = [], []
+    for q, k in ((full.inp["q"], full.inp["k"]), (s1["q"], s1["k"])):
+        q, k = q.to(DEV), k.to(DEV)
+        qh, kh = torch.empty_like(q), torch.empty_like(k)
+        ws.append(saq.qknorm_rope_pool(q, k, qh, kh, pos, (wq, wk), c.sections, c.rope_base, c.eps, c.block))
+        masks.append(saq.select_blocks_pooled(q.shape, keep, ws[-1], c.block))
+        del q, k, qh, kh
+    shape = (c.B, c.S, c.H, c.D)
+    out = saq.pooled_change(ws[0], ws[1], shape, c.block)
+    counts = saq.mask_overlap(masks[1], masks[0])
+    torch.cuda.synchronize()
+    npool = saq.pooled_bytes(*shape, c.block)
+    p0 = ws[0][:npool].view(torch.float64).cpu().numpy()
+    p1 = ws[1][:npool].view(torch.float64).cpu().numpy()
+    d2_ref, p2_ref = oracle.pooled_change(p0, p1)
+    d2, p2 = out[:2].tolist()
+    assert abs(d2 - d2_ref) <= 1e-12 * d2_ref and abs(p2 - p2_ref) <= 1e-12 * p2_ref
+    m0, m1 = masks[0].cpu().numpy(), masks[1].cpu().numpy()
+    assert np.array_equal(counts.cpu().numpy(), oracle.mask_overlap(m1, m0))
+    r = (d2 / p2) ** 0.5
+    ov = counts[..., 0].sum().item() / counts[..., 1].sum().item()
+    log(f"  full sweep step 0 -> 1: relative pooled change {r:.5f}, mask overlap {ov:.4f} at keep={keep}")
+    for thr, kept in ((2.0 * r, True), (0.5 * r, False)):
+        reuse = saq.MaskReuse(shape, keep, thr, c.block, DEV)
+        reuse.step(ws[0])
+        m = reuse.step(ws[1])
+        torch.cuda.synchronize()
+        assert reuse.recomputed() != kept
+        assert torch.equal(m, masks[0] if kept else masks[1])

@@ -51,3 +51,14 @@ def test_sweep_step0_equals_base():
                                                                    "drift": 0.05}), 3, tensors=("k",))
     d = (c["k"].float() - b["k"].float())
     assert 0.1 < d.std().item() < 0.2                  # 0.05 * 3 * N(0,1) plus bf16 rounding
+
+
+def test_sweep_composition_matches_host_generator():
+    import dataclasses
+    cfg = dataclasses.replace(synth.get_config("small"), name="small_sweep", steps=8, drift=0.05)
+    for name in ("q", "v"):
+        base, delta = synth.sweep_parts(cfg, name)
+        for step in (0, 1, 7):
+            ref = synth.make_sweep_inputs(cfg, step, tensors=(name,))[name]
+            got = synth.compose_sweep_step(base, delta, cfg.drift, step)
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), (name, step)
