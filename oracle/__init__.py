@@ -31,6 +31,10 @@ What it computes, in the order of the layer:
    overlap of two steps' masks and the relative change of their pooled block
    means, the detector that gates reusing a mask (cross-step cache paragraph of
    the "H3 on device" page).
+6. INT8 / FP8 block codecs (``oracle.codecs``): per-(token block, head) scaled
+   quantise/dequantise of the attention exchange's inputs (INT8) and outputs
+   (OCP E4M3), the transfer formats of multi-GPU Sol-Attn (KOCPC article on
+   Sol-H3, "Technical Composition").
 
 Every function is pinned by CPU tests to something other than itself: closed
 forms, invariants, library routines (complex multiplication, logspace,
@@ -44,11 +48,12 @@ from .prologue import qknorm, rope_inv_freq, rope_3d, qknorm_rope
 from .selection import (num_kept_blocks, pool_blocks, block_scores, select_topk,
                         select_blocks, block_token_range)
 from .attention import block_sparse_attention, block_sparse_attention_rows, dense_attention
+from . import codecs
 from .step_reuse import mask_overlap, pooled_change, relative_change, keeps_mask, reuse_schedule
 
 __all__ = [
     "qknorm", "rope_inv_freq", "rope_3d", "qknorm_rope",
     "num_kept_blocks", "pool_blocks", "block_scores", "select_topk", "select_blocks",
     "block_token_range", "block_sparse_attention", "block_sparse_attention_rows", "dense_attention",
-    "mask_overlap", "pooled_change", "relative_change", "keeps_mask", "reuse_schedule",
+    "mask_overlap", "pooled_change", "relative_change", "keeps_mask", "reuse_schedule", "codecs",
 ]
