@@ -258,14 +258,105 @@ def sweep(args) -> dict:
             "keeps": keeps, "thresholds": thresholds, "per_step": per_step, "summary": summary}
 
 
+def codec_bench(args) -> dict:
+    """The INT8 / FP8 block codecs on the full layer's tensors: per-kernel time and HBM rate (algorithmic bytes:
+    quantise reads 2 and writes 1 byte per element, dequantise the reverse, plus 4 bytes of scale per tile), and the
+    end-to-end effect of the exchange formats: the layer recomputed from INT8-decoded q-hat/k-hat/v (selection
+    included) against the bf16 layer, and the FP8 round trip of the output."""
+    import torch
+
+    import sparse_attention_qknorm_amd as saq
+    from sparse_attention_qknorm_amd import synth
+
+    cfg = synth.get_config("full")
+    keep = args.keep if args.keep is not None else cfg.keep_ratios[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    saq.lib()
+    log(f"[codecs] generating {cfg.name} inputs")
+    inp = synth.make_inputs(cfg)
+    q0, k0, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    pos, wq, wk = inp["pos_thw"].to(dev), inp["w_q"].to(dev), inp["w_k"].to(dev)
+    qh, kh = torch.empty_like(q0), torch.empty_like(k0)
+    ws = saq.qknorm_rope_pool(q0, k0, qh, kh, pos, (wq, wk), cfg.sections, cfg.rope_base, cfg.eps, cfg.block)
+    mask = saq.select_blocks_pooled(qh.shape, keep, ws, cfg.block)
+    o = saq.block_sparse_attn(qh, kh, v, mask, cfg.block)
+    B, S, H, D = qh.shape
+    n = B * S * H * D
+    tiles = B * cfg.nB * H
+    stream = torch.cuda.current_stream(dev)
+    bufs = {f: (torch.empty(qh.shape, dtype=torch.int8 if f == "int8" else torch.uint8, device=dev),
+                torch.empty((B, H, cfg.nB), dtype=torch.float32, device=dev)) for f in ("int8", "fp8")}
+    y = torch.empty_like(qh)
+
+    def time_call(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    res = {}
+    for fmt, src in (("int8", qh), ("fp8", o)):
+        c, sc = bufs[fmt]
+        tq = time_call(lambda: saq.quantize(src, fmt, cfg.block, codes=c, scales=sc), args.steps)
+        td = time_call(lambda: saq.dequantize(c, sc, fmt, cfg.block, out=y), args.steps)
+        qbytes = 3.0 * n + 4.0 * tiles
+        res[fmt] = {"quantize_ms": tq, "dequantize_ms": td,
+                    "quantize_gbs": qbytes / (tq / 1e3) / 1e9, "dequantize_gbs": qbytes / (td / 1e3) / 1e9,
+                    "quantize_frac_of_hbm_peak": qbytes / (tq / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    "dequantize_frac_of_hbm_peak": qbytes / (td / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    "algorithmic_bytes_per_launch": qbytes,
+                    "tensor": "q_hat" if fmt == "int8" else "attention output o"}
+        log(f"[codecs] {fmt}: quantize {tq:.3f} ms ({res[fmt]['quantize_gbs']:.0f} GB/s), "
+            f"dequantize {td:.3f} ms ({res[fmt]['dequantize_gbs']:.0f} GB/s)")
+
+    # end to end: the layer from INT8-decoded q-hat/k-hat/v, and the FP8 round trip of o
+    dq = {}
+    for name, t in (("q", qh), ("k", kh), ("v", v)):
+        c, sc = saq.quantize(t, "int8", cfg.block)
+        dq[name] = saq.dequantize(c, sc, "int8", cfg.block)
+        del c, sc
+    ws8 = torch.empty_like(ws)
+    m8 = saq.select_blocks(dq["q"], dq["k"], keep, cfg.block, workspace=ws8)
+    o8 = saq.block_sparse_attn(dq["q"], dq["k"], dq["v"], m8, cfg.block)
+    counts = saq.mask_overlap(m8, mask)
+    c, sc = saq.quantize(o, "fp8", cfg.block)
+    of8 = saq.dequantize(c, sc, "fp8", cfg.block)
+    torch.cuda.synchronize()
+
+    def errs(a, b):
+        d = a.float() - b.float()
+        return {"max_abs": float(d.abs().max().item()), "rel_fro": float(d.norm().item() / b.float().norm().item())}
+
+    cs = counts.sum(dim=(0, 1)).tolist()
+    res["int8_qkv_layer"] = {"mask_overlap_with_bf16_mask": cs[0] / cs[1], "o_vs_bf16_layer": errs(o8, o)}
+    res["fp8_o_roundtrip"] = errs(of8, o)
+    log(f"[codecs] INT8 q/k/v layer: mask overlap {cs[0] / cs[1]:.4f}, o error {res['int8_qkv_layer']['o_vs_bf16_layer']}; "
+        f"FP8 o round trip {res['fp8_o_roundtrip']}")
+    return {"metric": "INT8 QKV / FP8 O block codecs: GB/s per kernel and error of the exchange formats",
+            "n_gpus": 1, "data": "synthetic", "steps": args.steps, "warmup": args.warmup,
+            "config": {"workload": f"full layer tensors [1, {S}, {H}, {D}], tile = {cfg.block} tokens x {D} "
+                                   f"channels of one head, keep_ratio={keep}"},
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "achieved": res["int8"]["quantize_gbs"], "frac": res["int8"]["quantize_frac_of_hbm_peak"],
+                         "kernel": "quantize_kernel<128,128,int8>", "traffic": None},
+            **res}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="full", choices=["full", "medium", "small", "tiny", "sweep"],
-                    help="sweep: the 8-step drift sweep with gated mask reuse (a measurement of the reuse gate, "
-                         "printed as its own JSON line)")
+    ap.add_argument("--workload", default="full", choices=["full", "medium", "small", "tiny", "sweep", "codecs"],
+                    help="sweep: the 8-step drift sweep with gated mask reuse; codecs: the INT8/FP8 block "
+                         "codecs on the full layer's tensors (each a separate measurement, printed as its own JSON "
+                         "line)")
     ap.add_argument("--reuse-thresholds", default="0.005,0.01,0.02,0.04",
                     help="sweep only: relative pooled-change thresholds of the mask-reuse gate")
     ap.add_argument("--keep", type=float, default=None, help="keep ratio (default: the config's first)")
@@ -284,6 +375,9 @@ def main(argv=None) -> int:
               "heads; see the design notes). Run with --gpus 1.", file=sys.stderr)
         return 2
 
+    if args.workload == "codecs":
+        print(json.dumps(codec_bench(args)), flush=True)
+        return 0
     if args.workload == "sweep":
         print(json.dumps({"metric": "mask reuse across denoising steps (gate decisions, overlap, output error)",
                           "n_gpus": 1, "data": "synthetic", **sweep(args)}), flush=True)

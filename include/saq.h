@@ -178,7 +178,8 @@ int saq_select_blocks_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t
  *
  * saq_mask_overlap: for two masks [B,H,nB,nB] (non-zero byte = kept), writes
  * counts[2*(b*H+h)] = #(kept in both), counts[2*(b*H+h)+1] = #(kept in a).
- * counts: device int64 [2*B*H]. Exact integers.
+ * counts: device int64 [2*B*H], 8-byte aligned; masks 16-byte aligned;
+ * B*H <= 65535. Exact integers.
  *
  * saq_pooled_change: the change detector on the pooled block means that
  * saq_qknorm_rope_pool leaves in a selection workspace. With P = all 2*B*H*nB*D
@@ -227,6 +228,36 @@ int saq_select_blocks_reuse(int32_t B, int32_t S, int32_t H, int32_t D, int32_t 
                             double threshold, int32_t force, uint8_t* block_mask, void* workspace,
                             size_t workspace_bytes, void* pooled_ref, size_t pooled_ref_bytes, double* state,
                             size_t state_len, void* stream);
+
+/*
+ * INT8 / FP8 block codecs: the two ends of the multi-GPU attention exchange,
+ * whose inputs travel as INT8 and outputs as FP8 (KOCPC article on Sol-H3,
+ * "Technical Composition"). Encode a bf16 tensor [B,S,H,D] into one byte per
+ * element (same layout) plus one fp32 scale per (batch, token block, head)
+ * tile, scales laid out [B,H,nB]; decode back to bf16.
+ *
+ * A tile is tokens [i*block, min((i+1)*block, S)) of one head over all D
+ * channels. With amax = max |x| over the tile and Q = 127 (INT8) or 448 (FP8):
+ * inv = Q / amax and s = amax / Q (correctly rounded fp32 divisions); each x
+ * becomes round-to-nearest-even of the fp32 product x * inv, as an integer
+ * clamped to [-127, 127] (INT8) or as the nearest OCP E4M3 value (FP8: bias 7,
+ * no infinities, largest finite 448; the tile's amax maps to +-Q, so nothing
+ * overflows). A tile with amax < 2^-100 stores s = 0 and zero codes. Decoding:
+ * bf16 round-to-nearest-even of the fp32 product value(code) * s.
+ *
+ *   x, y      bf16 [B,S,H,D], 16-byte aligned; finite values (others undefined)
+ *   codes     1 byte per element, [B,S,H,D], 8-byte aligned
+ *   scales    fp32 [B,H,nB], 4-byte aligned (written by quantize, read by dequantize)
+ *   D and block in {64, 128}. No buffer may overlap another (SAQ_ERR_ALIAS).
+ */
+int saq_quantize_int8(const void* x, int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, int8_t* codes,
+                      float* scales, void* stream);
+int saq_dequantize_int8(const int8_t* codes, const float* scales, int32_t B, int32_t S, int32_t H, int32_t D,
+                        int32_t block, void* y, void* stream);
+int saq_quantize_fp8(const void* x, int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, uint8_t* codes,
+                     float* scales, void* stream);
+int saq_dequantize_fp8(const uint8_t* codes, const float* scales, int32_t B, int32_t S, int32_t H, int32_t D,
+                       int32_t block, void* y, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* saq_status_string(int status);

@@ -13,7 +13,9 @@ variant. Readings taken here:
   Q = 127 (INT8) or 448 (FP8): inv = fl32(Q / amax), the stored scale
   s = fl32(amax / Q), and each x encodes as round-to-nearest-even of
   fl32(x * inv) (an integer clamped to [-Q, Q] for INT8, the nearest E4M3
-  value for FP8); an all-zero tile has inv = s = 0 and all codes 0;
+  value for FP8); a tile with amax < 2^-100 (all zero, or so small that inv
+  would overflow fp32) has inv = s = 0, so every code is a zero (FP8 keeps
+  the sign of x: x * 0 is a signed zero);
 * decoding is fl32(value(code) * s), rounded to bf16 nearest-even.
 
 The codes are integer decisions taken from floating point, so this oracle takes
@@ -73,8 +75,11 @@ def _tiles(S: int, block: int):
         yield i, i * block, min(S, (i + 1) * block)
 
 
+TINY_AMAX = 2.0 ** -100
+
+
 def _scale_pair(amax: np.float32, qmax: float):
-    if amax == 0:
+    if amax < TINY_AMAX:
         return np.float32(0.0), np.float32(0.0)
     q = np.float32(qmax)
     return np.float32(q / amax), np.float32(amax / q)

@@ -23,7 +23,7 @@ from ._binding import SaqError, check, lib
 
 __all__ = ["qknorm_rope", "qknorm_rope_out", "qknorm_rope_pool", "select_blocks", "select_blocks_pooled",
            "select_workspace_bytes", "block_sparse_attn", "kept_blocks", "mask_overlap", "pooled_change", "pooled_bytes",
-           "MaskReuse", "SaqError", "lib"]
+           "MaskReuse", "quantize", "dequantize", "SaqError", "lib"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -241,3 +241,44 @@ class MaskReuse:
     def relative_change(self) -> float:
         d2, p2 = self.state[:2].tolist()
         return (d2 / p2) ** 0.5 if p2 > 0 else (0.0 if d2 == 0 else float("inf"))
+
+
+def quantize(x: torch.Tensor, fmt: str, block: int = 128, codes: Optional[torch.Tensor] = None,
+             scales: Optional[torch.Tensor] = None):
+    """Block-scaled INT8 (fmt="int8") or OCP E4M3 (fmt="fp8") codes of a bf16 [B,S,H,D] tensor: (codes [B,S,H,D]
+    int8 / uint8, scales fp32 [B,H,nB]) (saq_quantize_int8 / saq_quantize_fp8)."""
+    _check_qkv("x", x)
+    B, S, H, D = x.shape
+    nB = -(-S // block)
+    cdt = {"int8": torch.int8, "fp8": torch.uint8}[fmt]
+    if codes is None:
+        codes = torch.empty((B, S, H, D), dtype=cdt, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, nB), dtype=torch.float32, device=x.device)
+    if codes.dtype != cdt or tuple(codes.shape) != (B, S, H, D) or not codes.is_contiguous():
+        raise ValueError(f"codes must be a contiguous {cdt} [B,S,H,D] tensor")
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (B, H, nB) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous float32 [B,H,nB] tensor")
+    fn = lib().saq_quantize_int8 if fmt == "int8" else lib().saq_quantize_fp8
+    check(fn(x.data_ptr(), B, S, H, D, block, codes.data_ptr(), scales.data_ptr(), _stream(x)),
+          f"saq_quantize_{fmt}")
+    return codes, scales
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: str, block: int = 128,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [B,S,H,D] from block-scaled codes (saq_dequantize_int8 / saq_dequantize_fp8)."""
+    cdt = {"int8": torch.int8, "fp8": torch.uint8}[fmt]
+    if codes.dtype != cdt or codes.dim() != 4 or not codes.is_contiguous() or not codes.is_cuda:
+        raise ValueError(f"codes must be a contiguous {cdt} [B,S,H,D] device tensor")
+    B, S, H, D = codes.shape
+    nB = -(-S // block)
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (B, H, nB) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous float32 [B,H,nB] tensor")
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=codes.device)
+    _check_qkv("out", out)
+    fn = lib().saq_dequantize_int8 if fmt == "int8" else lib().saq_dequantize_fp8
+    check(fn(codes.data_ptr(), scales.data_ptr(), B, S, H, D, block, out.data_ptr(), _stream(codes)),
+          f"saq_dequantize_{fmt}")
+    return out

@@ -22,7 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsaq.so")
 
-SOURCES = ["capi.hip", "qknorm_rope.hip", "select_blocks.hip", "block_sparse_attn.hip", "step_reuse.hip"]
+SOURCES = ["capi.hip", "qknorm_rope.hip", "select_blocks.hip", "block_sparse_attn.hip", "step_reuse.hip",
+           "codecs.hip"]
 ARCH = os.environ.get("SAQ_OFFLOAD_ARCH", "gfx950")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 

@@ -154,8 +154,8 @@ int saq_select_blocks_pooled(int32_t B, int32_t S, int32_t H, int32_t D, int32_t
 int saq_mask_overlap(const uint8_t* mask_a, const uint8_t* mask_b, int32_t B, int32_t H, int32_t nB,
                      int64_t* counts, void* stream) {
     if (!mask_a || !mask_b || !counts) return SAQ_ERR_NULL;
-    if (B < 1 || H < 1 || nB < 1 || nB > saq::kMaxBlocks) return SAQ_ERR_SHAPE;
-    if (((uintptr_t)counts & 7u) != 0) return SAQ_ERR_ALIGN;
+    if (B < 1 || H < 1 || nB < 1 || nB > saq::kMaxBlocks || (int64_t)B * H > 65535) return SAQ_ERR_SHAPE;
+    if (((uintptr_t)counts & 7u) != 0 || !aligned16(mask_a) || !aligned16(mask_b)) return SAQ_ERR_ALIGN;
     const size_t mbytes = (size_t)B * H * nB * nB;
     if (overlaps(counts, (size_t)B * H * 16, mask_a, mbytes) || overlaps(counts, (size_t)B * H * 16, mask_b, mbytes))
         return SAQ_ERR_ALIAS;
@@ -223,6 +223,57 @@ int saq_select_blocks_reuse(int32_t B, int32_t S, int32_t H, int32_t D, int32_t 
     if (st) return st;
     return finish(saq::launch_select_reuse(B, S, H, D, block, kept, workspace, (double*)pooled_ref, threshold,
                                            force != 0 ? 1 : 0, block_mask, state, (hipStream_t)stream));
+}
+
+static int validate_codec(const void* bf, const void* codes, const float* scales, int32_t B, int32_t S, int32_t H,
+                          int32_t D, int32_t block) {
+    if (!bf || !codes || !scales) return SAQ_ERR_NULL;
+    int st = check_dims(B, S, H, D);
+    if (st) return st;
+    st = check_block(S, block);
+    if (st) return st;
+    const int64_t nB = ((int64_t)S + block - 1) / block;
+    if ((int64_t)B * nB * H >= ((int64_t)1 << 31)) return SAQ_ERR_SHAPE;
+    if (!aligned16(bf) || ((uintptr_t)codes & 7u) != 0 || ((uintptr_t)scales & 3u) != 0) return SAQ_ERR_ALIGN;
+    const size_t n = (size_t)B * S * H * D;
+    const size_t sbytes = (size_t)B * H * nB * sizeof(float);
+    if (overlaps(bf, n * 2, codes, n) || overlaps(bf, n * 2, scales, sbytes) || overlaps(codes, n, scales, sbytes))
+        return SAQ_ERR_ALIAS;
+    return device_ready();
+}
+
+static int quantize_entry(bool fp8, const void* x, int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
+                          void* codes, float* scales, void* stream) {
+    const int st = validate_codec(x, codes, scales, B, S, H, D, block);
+    if (st) return st;
+    return finish(saq::launch_quantize(fp8, x, codes, scales, B, S, H, D, block, (hipStream_t)stream));
+}
+
+static int dequantize_entry(bool fp8, const void* codes, const float* scales, int32_t B, int32_t S, int32_t H,
+                            int32_t D, int32_t block, void* y, void* stream) {
+    const int st = validate_codec(y, codes, scales, B, S, H, D, block);
+    if (st) return st;
+    return finish(saq::launch_dequantize(fp8, codes, scales, y, B, S, H, D, block, (hipStream_t)stream));
+}
+
+int saq_quantize_int8(const void* x, int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, int8_t* codes,
+                      float* scales, void* stream) {
+    return quantize_entry(false, x, B, S, H, D, block, codes, scales, stream);
+}
+
+int saq_dequantize_int8(const int8_t* codes, const float* scales, int32_t B, int32_t S, int32_t H, int32_t D,
+                        int32_t block, void* y, void* stream) {
+    return dequantize_entry(false, codes, scales, B, S, H, D, block, y, stream);
+}
+
+int saq_quantize_fp8(const void* x, int32_t B, int32_t S, int32_t H, int32_t D, int32_t block, uint8_t* codes,
+                     float* scales, void* stream) {
+    return quantize_entry(true, x, B, S, H, D, block, codes, scales, stream);
+}
+
+int saq_dequantize_fp8(const uint8_t* codes, const float* scales, int32_t B, int32_t S, int32_t H, int32_t D,
+                       int32_t block, void* y, void* stream) {
+    return dequantize_entry(true, codes, scales, B, S, H, D, block, y, stream);
 }
 
 int32_t saq_kept_blocks(double keep_ratio, int32_t nB) {

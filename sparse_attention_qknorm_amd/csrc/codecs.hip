@@ -1,0 +1,239 @@
+// INT8 / FP8 block codecs for the attention exchange.
+//
+// Multi-GPU Sol-Attn ships attention inputs as INT8 and outputs as FP8 (KOCPC
+// article on Sol-H3, "Technical Composition"). These kernels are the two ends
+// of that exchange on one GPU: bf16 [B,S,H,D] <-> codes of the same layout plus
+// one fp32 scale per (batch, token block, head) tile, stored [B,H,nB].
+//
+// Encoding of a tile with amax = max |x| (an exact bf16 value) and Q = 127
+// (INT8) or 448 (FP8, OCP E4M3): inv = Q / amax and s = amax / Q, both
+// correctly rounded fp32 divisions (one pair per tile); every element becomes
+// round-to-nearest-even of the fp32 product x * inv, an integer clamped to
+// [-Q, Q] for INT8, the nearest E4M3 value for FP8 (hardware conversion). A
+// tile with amax < 2^-100 (all zero, or so small that inv would overflow)
+// stores s = 0 and encodes x * 0 (a zero; FP8 keeps its sign). Decoding is the fp32 product
+// value(code) * s rounded to bf16 nearest-even.
+//
+// Memory-bound (2 bytes read + 1 written per element, or the reverse): one
+// workgroup per tile, heads fastest in the launch order so that neighbouring
+// workgroups stream neighbouring bytes of the same token rows; each thread keeps
+// its chunks of the tile in registers between the amax pass and the encode pass,
+// so the input is read once.
+#include "common.h"
+#include "kernels.h"
+
+namespace saq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D, int BLOCK>
+struct Tile {
+    static constexpr int kChunksPerRow = D / 8;             // 8 elements per 16-byte bf16 chunk
+    static constexpr int kPer = BLOCK * kChunksPerRow / kThreads;
+    static_assert(kPer >= 1 && BLOCK * kChunksPerRow % kThreads == 0, "tile must split evenly");
+};
+
+struct TileIndex {
+    int32_t b, i, h, t0, n;
+};
+
+__device__ __forceinline__ TileIndex tile_index(int32_t S, int32_t H, int32_t nB, int32_t block) {
+    TileIndex t;
+    const int64_t w = blockIdx.x;
+    t.h = (int32_t)(w % H);
+    const int64_t bi = w / H;
+    t.i = (int32_t)(bi % nB);
+    t.b = (int32_t)(bi / nB);
+    t.t0 = t.i * block;
+    t.n = min(block, S - t.t0);
+    return t;
+}
+
+__device__ __forceinline__ uint32_t abs_max_bits(uint32_t acc, uint32_t w) {
+    // |bf16| orders like its low 15 bits read as an unsigned integer (finite inputs)
+    acc = max(acc, w & 0x7fffu);
+    return max(acc, (w >> 16) & 0x7fffu);
+}
+
+__device__ __forceinline__ uint32_t encode_int8x4(float a, float b, float c, float d) {
+    const float lo = -127.0f, hi = 127.0f;
+    const int32_t qa = (int32_t)fminf(fmaxf(__builtin_rintf(a), lo), hi);
+    const int32_t qb = (int32_t)fminf(fmaxf(__builtin_rintf(b), lo), hi);
+    const int32_t qc = (int32_t)fminf(fmaxf(__builtin_rintf(c), lo), hi);
+    const int32_t qd = (int32_t)fminf(fmaxf(__builtin_rintf(d), lo), hi);
+    return (uint32_t)(qa & 0xff) | ((uint32_t)(qb & 0xff) << 8) | ((uint32_t)(qc & 0xff) << 16) |
+           ((uint32_t)(qd & 0xff) << 24);
+}
+
+__device__ __forceinline__ uint32_t encode_fp8x4(float a, float b, float c, float d) {
+    int32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);        // bytes 0, 1
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);                 // bytes 2, 3
+    return (uint32_t)r;
+}
+
+template <int D, int BLOCK, bool FP8>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restrict__ x, uint2* __restrict__ codes,
+                                                            float* __restrict__ scales, int32_t S, int32_t H,
+                                                            int32_t nB) {
+#pragma clang fp contract(off)
+    using T = Tile<D, BLOCK>;
+    __shared__ uint32_t red[kThreads / kWave];
+    const TileIndex t = tile_index(S, H, nB, BLOCK);
+    const int64_t row0 = ((int64_t)t.b * S + t.t0) * H + t.h;       // (token t0, head h) row
+    uint4 v[T::kPer];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < T::kPer; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        const int r = c / T::kChunksPerRow;
+        const int cc = c % T::kChunksPerRow;
+        if (r < t.n) {
+            v[j] = x[(row0 + (int64_t)r * H) * T::kChunksPerRow + cc];
+            amax = abs_max_bits(amax, v[j].x);
+            amax = abs_max_bits(amax, v[j].y);
+            amax = abs_max_bits(amax, v[j].z);
+            amax = abs_max_bits(amax, v[j].w);
+        } else {
+            v[j] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    for (int off = kWave / 2; off >= 1; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) amax = max(amax, red[w]);
+
+    constexpr float kQ = FP8 ? 448.0f : 127.0f;
+    const float a = bf16_bits_to_f32(amax);
+    float inv = 0.0f, s = 0.0f;
+    if (a >= 0x1p-100f) {                                  // below: a zero tile (inv would overflow)
+        inv = kQ / a;
+        s = a / kQ;
+    }
+    if (threadIdx.x == 0) scales[((int64_t)t.b * H + t.h) * nB + t.i] = s;
+
+#pragma unroll
+    for (int j = 0; j < T::kPer; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        const int r = c / T::kChunksPerRow;
+        const int cc = c % T::kChunksPerRow;
+        if (r >= t.n) continue;
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p[2 * e] = __uint_as_float(w[e] << 16) * inv;
+            p[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u) * inv;
+        }
+        uint2 out;
+        if (FP8) {
+            out.x = encode_fp8x4(p[0], p[1], p[2], p[3]);
+            out.y = encode_fp8x4(p[4], p[5], p[6], p[7]);
+        } else {
+            out.x = encode_int8x4(p[0], p[1], p[2], p[3]);
+            out.y = encode_int8x4(p[4], p[5], p[6], p[7]);
+        }
+        codes[(row0 + (int64_t)r * H) * T::kChunksPerRow + cc] = out;
+    }
+}
+
+__device__ __forceinline__ float decode_int8(uint32_t w, int byte) {
+    return (float)(int32_t)(int8_t)((w >> (8 * byte)) & 0xff);
+}
+
+template <int D, int BLOCK, bool FP8>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint2* __restrict__ codes,
+                                                              const float* __restrict__ scales,
+                                                              uint4* __restrict__ y, int32_t S, int32_t H,
+                                                              int32_t nB) {
+#pragma clang fp contract(off)
+    using T = Tile<D, BLOCK>;
+    const TileIndex t = tile_index(S, H, nB, BLOCK);
+    const int64_t row0 = ((int64_t)t.b * S + t.t0) * H + t.h;
+    const float s = scales[((int64_t)t.b * H + t.h) * nB + t.i];
+#pragma unroll
+    for (int j = 0; j < T::kPer; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        const int r = c / T::kChunksPerRow;
+        const int cc = c % T::kChunksPerRow;
+        if (r >= t.n) continue;
+        const int64_t idx = (row0 + (int64_t)r * H) * T::kChunksPerRow + cc;
+        const uint2 q = codes[idx];
+        const uint32_t w[2] = {q.x, q.y};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float f[4];
+            if (FP8) {
+                f[0] = __builtin_amdgcn_cvt_f32_fp8((int)w[e], 0);
+                f[1] = __builtin_amdgcn_cvt_f32_fp8((int)w[e], 1);
+                f[2] = __builtin_amdgcn_cvt_f32_fp8((int)w[e], 2);
+                f[3] = __builtin_amdgcn_cvt_f32_fp8((int)w[e], 3);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) f[k] = decode_int8(w[e], k);
+            }
+            o[2 * e] = f32_to_bf16_bits(f[0] * s) | (f32_to_bf16_bits(f[1] * s) << 16);
+            o[2 * e + 1] = f32_to_bf16_bits(f[2] * s) | (f32_to_bf16_bits(f[3] * s) << 16);
+        }
+        y[idx] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+template <bool FP8>
+hipError_t launch_quantize_t(const void* x, void* codes, float* scales, int32_t B, int32_t S, int32_t H, int32_t D,
+                             int32_t block, hipStream_t stream) {
+    const int32_t nB = (S + block - 1) / block;
+    const dim3 grid((unsigned)((int64_t)B * nB * H));
+    const uint4* xi = (const uint4*)x;
+    uint2* ci = (uint2*)codes;
+    if (D == 128 && block == 128)
+        hipLaunchKernelGGL((quantize_kernel<128, 128, FP8>), grid, dim3(kThreads), 0, stream, xi, ci, scales, S, H, nB);
+    else if (D == 128)
+        hipLaunchKernelGGL((quantize_kernel<128, 64, FP8>), grid, dim3(kThreads), 0, stream, xi, ci, scales, S, H, nB);
+    else if (block == 128)
+        hipLaunchKernelGGL((quantize_kernel<64, 128, FP8>), grid, dim3(kThreads), 0, stream, xi, ci, scales, S, H, nB);
+    else
+        hipLaunchKernelGGL((quantize_kernel<64, 64, FP8>), grid, dim3(kThreads), 0, stream, xi, ci, scales, S, H, nB);
+    return hipGetLastError();
+}
+
+template <bool FP8>
+hipError_t launch_dequantize_t(const void* codes, const float* scales, void* y, int32_t B, int32_t S, int32_t H,
+                               int32_t D, int32_t block, hipStream_t stream) {
+    const int32_t nB = (S + block - 1) / block;
+    const dim3 grid((unsigned)((int64_t)B * nB * H));
+    const uint2* ci = (const uint2*)codes;
+    uint4* yi = (uint4*)y;
+    if (D == 128 && block == 128)
+        hipLaunchKernelGGL((dequantize_kernel<128, 128, FP8>), grid, dim3(kThreads), 0, stream, ci, scales, yi, S, H,
+                           nB);
+    else if (D == 128)
+        hipLaunchKernelGGL((dequantize_kernel<128, 64, FP8>), grid, dim3(kThreads), 0, stream, ci, scales, yi, S, H,
+                           nB);
+    else if (block == 128)
+        hipLaunchKernelGGL((dequantize_kernel<64, 128, FP8>), grid, dim3(kThreads), 0, stream, ci, scales, yi, S, H,
+                           nB);
+    else
+        hipLaunchKernelGGL((dequantize_kernel<64, 64, FP8>), grid, dim3(kThreads), 0, stream, ci, scales, yi, S, H,
+                           nB);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(bool fp8, const void* x, void* codes, float* scales, int32_t B, int32_t S, int32_t H,
+                           int32_t D, int32_t block, hipStream_t stream) {
+    return fp8 ? launch_quantize_t<true>(x, codes, scales, B, S, H, D, block, stream)
+               : launch_quantize_t<false>(x, codes, scales, B, S, H, D, block, stream);
+}
+
+hipError_t launch_dequantize(bool fp8, const void* codes, const float* scales, void* y, int32_t B, int32_t S,
+                             int32_t H, int32_t D, int32_t block, hipStream_t stream) {
+    return fp8 ? launch_dequantize_t<true>(codes, scales, y, B, S, H, D, block, stream)
+               : launch_dequantize_t<false>(codes, scales, y, B, S, H, D, block, stream);
+}
+
+}  // namespace saq

@@ -78,3 +78,13 @@ hipError_t launch_select_reuse(int32_t B, int32_t S, int32_t H, int32_t D, int32
                                uint8_t* mask, double* state, hipStream_t stream);
 
 }  // namespace saq
+
+namespace saq {
+
+// INT8 / FP8 (OCP E4M3) block codecs (codecs.hip): codes [B,S,H,D] (1 byte each), scales fp32 [B,H,nB].
+hipError_t launch_quantize(bool fp8, const void* x, void* codes, float* scales, int32_t B, int32_t S, int32_t H,
+                           int32_t D, int32_t block, hipStream_t stream);
+hipError_t launch_dequantize(bool fp8, const void* codes, const float* scales, void* y, int32_t B, int32_t S,
+                             int32_t H, int32_t D, int32_t block, hipStream_t stream);
+
+}  // namespace saq

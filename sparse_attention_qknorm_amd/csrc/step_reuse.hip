@@ -31,18 +31,53 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// one workgroup per (b, h): the nB x nB bytes of both masks
+constexpr int kOverlapSplit = 16;     // workgroups per (b, h) for the overlap counts
+
+// high bit of each byte set iff that byte is non-zero
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
+    return (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
+}
+
+__global__ void zero_counts_kernel(int64_t* __restrict__ counts, int64_t n) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e < n) counts[e] = 0;
+}
+
+// grid (kOverlapSplit, B*H): workgroup g of head bh counts bytes [g*n/G, (g+1)*n/G) of that head's nB x nB
+// bytes, 16 at a time where the address allows it, and adds its integer totals atomically (exact, so the
+// result does not depend on the order).
 __global__ __launch_bounds__(kThreads) void mask_overlap_kernel(const uint8_t* __restrict__ a,
                                                                 const uint8_t* __restrict__ b, int64_t n_per_head,
                                                                 int64_t* __restrict__ counts) {
     __shared__ int64_t red[2][kThreads / kWave];
-    const int64_t bh = blockIdx.x;
-    const uint8_t* pa = a + bh * n_per_head;
-    const uint8_t* pb = b + bh * n_per_head;
+    const int64_t bh = blockIdx.y;
+    const int64_t lo = bh * n_per_head + n_per_head * blockIdx.x / kOverlapSplit;
+    const int64_t hi = bh * n_per_head + n_per_head * (blockIdx.x + 1) / kOverlapSplit;
     int64_t both = 0, na = 0;
-    // the head's bytes start at bh * nB^2, which may not be 4-byte aligned: read bytes
-    for (int64_t e = threadIdx.x; e < n_per_head; e += kThreads) {
-        const bool x = pa[e] != 0, y = pb[e] != 0;
+    // bytes up to the first 16-byte boundary (a and b share their alignment: same offsets, 16-aligned bases)
+    const int64_t vlo = min(hi, (lo + 15) & ~(int64_t)15);
+    const int64_t vhi = max(vlo, hi & ~(int64_t)15);
+    for (int64_t e = lo + threadIdx.x; e < vlo; e += kThreads) {
+        const bool x = a[e] != 0, y = b[e] != 0;
+        na += x;
+        both += x && y;
+    }
+    const uint4* a4 = (const uint4*)(a + vlo);
+    const uint4* b4 = (const uint4*)(b + vlo);
+    const int64_t n4 = (vhi - vlo) / 16;
+    for (int64_t e = threadIdx.x; e < n4; e += kThreads) {
+        const uint4 x = a4[e], y = b4[e];
+        const uint32_t ax[4] = {x.x, x.y, x.z, x.w};
+        const uint32_t by[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t nx = nonzero_bytes(ax[k]);
+            na += __popc(nx);
+            both += __popc(nx & nonzero_bytes(by[k]));
+        }
+    }
+    for (int64_t e = vhi + threadIdx.x; e < hi; e += kThreads) {
+        const bool x = a[e] != 0, y = b[e] != 0;
         na += x;
         both += x && y;
     }
@@ -61,8 +96,8 @@ __global__ __launch_bounds__(kThreads) void mask_overlap_kernel(const uint8_t* _
             s0 += red[0][w];
             s1 += red[1][w];
         }
-        counts[2 * bh] = s0;
-        counts[2 * bh + 1] = s1;
+        atomicAdd((unsigned long long*)&counts[2 * bh], (unsigned long long)s0);
+        atomicAdd((unsigned long long*)&counts[2 * bh + 1], (unsigned long long)s1);
     }
 }
 
@@ -140,8 +175,13 @@ __global__ __launch_bounds__(kThreads) void copy_if_kernel(const double2* __rest
 
 hipError_t launch_mask_overlap(const uint8_t* a, const uint8_t* b, int32_t B, int32_t H, int32_t nB, int64_t* counts,
                                hipStream_t stream) {
-    hipLaunchKernelGGL(mask_overlap_kernel, dim3((unsigned)((int64_t)B * H)), dim3(kThreads), 0, stream, a, b,
-                       (int64_t)nB * nB, counts);
+    const int64_t n = 2 * (int64_t)B * H;
+    hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                       counts, n);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(mask_overlap_kernel, dim3(kOverlapSplit, (unsigned)((int64_t)B * H)), dim3(kThreads), 0, stream,
+                       a, b, (int64_t)nB * nB, counts);
     return hipGetLastError();
 }
 

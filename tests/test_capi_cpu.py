@@ -172,6 +172,8 @@ def test_step_reuse_validation():
     assert lib.saq_mask_overlap(FAKE, None, 1, 2, 16, 1 << 24, None) == -1
     assert lib.saq_mask_overlap(FAKE, FAKE * 2, 1, 2, 0, 1 << 24, None) == -2
     assert lib.saq_mask_overlap(FAKE, FAKE * 2, 1, 2, 16, (1 << 24) + 4, None) == -4
+    assert lib.saq_mask_overlap(FAKE + 8, FAKE * 2, 1, 2, 16, 1 << 24, None) == -4
+    assert lib.saq_mask_overlap(FAKE, FAKE * 2, 1, 65536, 1, 1 << 24, None) == -2
 
 
 def test_fused_prologue_pool_validation():
@@ -195,3 +197,23 @@ def test_fused_prologue_pool_validation():
 
     assert sel(mask=None) == -1 and sel(keep=2.0) == -5 and sel(wbytes=0) == -6
     assert sel(mask=(1 << 24) + 64) == -9
+
+
+def test_codec_validation():
+    lib = _binding.lib()
+    # S=1024, H=2, D=64: x 256 KiB, codes 128 KiB, scales 2*16*4 = 128 B
+    x, codes, scales = 1 << 24, 1 << 25, 1 << 26
+
+    for q, d in ((lib.saq_quantize_int8, lib.saq_dequantize_int8), (lib.saq_quantize_fp8, lib.saq_dequantize_fp8)):
+        def qc(x=x, codes=codes, scales=scales, S=1024, D=64, block=64):
+            return q(x, 1, S, 2, D, block, codes, scales, None)
+
+        def dc(x=x, codes=codes, scales=scales, S=1024, D=64, block=64):
+            return d(codes, scales, 1, S, 2, D, block, x, None)
+
+        for f in (qc, dc):
+            assert f(x=None) == -1 and f(codes=None) == -1 and f(scales=None) == -1
+            assert f(S=0) == -2 and f(D=96) == -3 and f(block=32) == -3
+            assert f(x=x + 8) == -4 and f(codes=codes + 4) == -4 and f(scales=scales + 2) == -4
+            assert f(codes=x + 1024) == -9                 # codes inside x
+            assert f(scales=codes + 64) == -9              # scales inside codes

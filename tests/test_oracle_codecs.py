@@ -83,7 +83,7 @@ def test_quantize_tiles_and_bounds():
     for fmt, qmax in (("int8", 127), ("fp8", 448.0)):
         codes, scales = codecs.quantize(x, block, fmt)
         assert scales.shape == (B, H, 3)
-        assert scales[0, 1, 1] == 0.0 and not codes[0, 64:128, 1].any()
+        assert scales[0, 1, 1] == 0.0 and not codes[0, 64:128, 1].any()     # +0 inputs: +0 codes
         for b in range(B):
             for i, (t0, t1) in enumerate([(0, 64), (64, 128), (128, 150)]):
                 for h in range(H):
@@ -125,3 +125,20 @@ def test_fp8_full_range_tile_is_the_format_itself():
     codes, scales = codecs.quantize(x, 4096, "fp8")
     assert (scales == 1.0).all()
     assert np.array_equal(codes.ravel(), _torch_e4m3(x.ravel()))
+
+
+def test_tiny_tiles_are_zero_tiles():
+    x = np.zeros((1, 4, 1, 8), dtype=np.float32)
+    x[0, :, 0, 0] = [2.0 ** -101, -2.0 ** -110, 0.0, 2.0 ** -120]   # amax < 2^-100
+    x[0, :, 0, 1] = 0.0
+    for fmt in ("int8", "fp8"):
+        codes, scales = codecs.quantize(x, 64, fmt)
+        vals = codes if fmt == "int8" else codecs.e4m3_decode(codes)
+        assert scales.tolist() == [[[0.0]]] and not vals.any()            # zeros (FP8 keeps the sign of x)
+        x2 = x.copy()
+        x2[0, 0, 0, 0] = 2.0 ** -100                                  # at the limit: a real scale, finite inv
+        codes, scales = codecs.quantize(x2, 64, fmt)
+        q = 127 if fmt == "int8" else 448.0
+        assert scales[0, 0, 0] == np.float32(np.float32(2.0 ** -100) / np.float32(q)) and np.isfinite(scales).all()
+        v = codes[0, 0, 0, 0] if fmt == "int8" else codecs.e4m3_decode(codes[0, 0, 0, 0])
+        assert v == q
