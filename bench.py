@@ -360,9 +360,11 @@ def main(argv=None) -> int:
     ap.add_argument("--reuse-thresholds", default="0.005,0.01,0.02,0.04",
                     help="sweep only: relative pooled-change thresholds of the mask-reuse gate")
     ap.add_argument("--keep", type=float, default=None, help="keep ratio (default: the config's first)")
-    ap.add_argument("--path", default="fused", choices=["fused", "split"],
+    ap.add_argument("--path", default="fused", choices=["fused", "split", "folded"],
                     help="fused: prologue with block pooling folded in, then selection from the pooled vectors; "
-                         "split: the three separate calls qknorm_rope / select_blocks / block_sparse_attn")
+                         "split: the three separate calls qknorm_rope / select_blocks / block_sparse_attn; "
+                         "folded: fused prologue, then attention with the selection inside the kernel "
+                         "(block_sparse_attn_select)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention in the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -414,7 +416,7 @@ def main(argv=None) -> int:
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record(stream)
-        if args.path == "fused":
+        if args.path in ("fused", "folded"):
             saq.qknorm_rope_pool(q0, k0, qh, kh, pos, (wq, wk), cfg.sections, cfg.rope_base, cfg.eps, cfg.block,
                                  workspace=ws)
         else:
@@ -423,11 +425,16 @@ def main(argv=None) -> int:
             e[1].record(stream)
         if args.path == "fused":
             saq.select_blocks_pooled(qh.shape, keep, ws, cfg.block, out=mask)
-        else:
+        elif args.path == "split":
             saq.select_blocks(qh, kh, keep, cfg.block, out=mask, workspace=ws)
         if record:
             e[2].record(stream)
-        saq.block_sparse_attn(qh, kh, v, mask, cfg.block, out=o)
+        if args.path == "folded":
+            # the selection runs inside the attention kernel; the mask is written only on the first
+            # (untimed) call, for the FLOP count
+            saq.block_sparse_attn_select(qh, kh, v, ws, keep, cfg.block, out=o, mask_out=None if record else mask)
+        else:
+            saq.block_sparse_attn(qh, kh, v, mask, cfg.block, out=o)
         if record:
             e[3].record(stream)
             ev["pro"].append((e[0], e[1]))
@@ -483,6 +490,8 @@ def main(argv=None) -> int:
         "path": args.path,
         "ms_per_call": ({"qknorm_rope_pool": ms["pro"], "select_blocks_pooled": ms["sel"],
                          "block_sparse_attn": ms["att"]} if args.path == "fused" else
+                        {"qknorm_rope_pool": ms["pro"], "block_sparse_attn_select": ms["att"]}
+                        if args.path == "folded" else
                         {"qknorm_rope": ms["pro"], "select_blocks": ms["sel"], "block_sparse_attn": ms["att"]}),
         "attention_tflops_computed": achieved,
         "attention_tflops_dense_equivalent": dense_flops / att_s / 1e12,
@@ -492,7 +501,9 @@ def main(argv=None) -> int:
         "prologue_gbs": pro_bytes / (ms["pro"] / 1e3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic,
-                     "kernel": "d128::attn_kernel (block 128, head_dim 128)", "kernel_hash": khash,
+                     "kernel": ("d128::attn_kernel<false> (block 128, head_dim 128)" if args.path != "folded" else
+                                "d128::attn_kernel<true> (block 128, head_dim 128, selection folded in)"),
+                     "kernel_hash": khash,
                      "flop_per_launch": flops},
     }
     if args.copy_calibration:

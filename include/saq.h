@@ -259,6 +259,28 @@ int saq_quantize_fp8(const void* x, int32_t B, int32_t S, int32_t H, int32_t D, 
 int saq_dequantize_fp8(const uint8_t* codes, const float* scales, int32_t B, int32_t S, int32_t H, int32_t D,
                        int32_t block, void* y, void* stream);
 
+/*
+ * Block-sparse attention with the block selection folded into the attention
+ * pass: no separate routing stage and no mask in memory (the Sol-Attn
+ * paragraph of the "H3 on device" page describes the selection as part of the
+ * online-softmax pass; its rule is not given, so the rule is the one of
+ * saq_select_blocks). Each workgroup scores its query block against every key
+ * block from the pooled means that saq_qknorm_rope_pool left in `workspace`,
+ * keeps the diagonal and the k-1 best (k = saq_kept_blocks(keep_ratio, nB)),
+ * and attends over them. The mask and the output are bit-identical to
+ * saq_select_blocks_pooled followed by saq_block_sparse_attn.
+ *
+ *   workspace       as written by saq_qknorm_rope_pool for these q, k (only its
+ *                   pooled part, 2*B*H*nB*D doubles, is read); 256-byte aligned
+ *   block_mask_out  optional uint8 [B,H,nB,nB]: the rows chosen (null: not written)
+ *   D = block = 128 only (SAQ_ERR_UNSUPPORTED otherwise); other arguments,
+ *   layouts and aliasing rules as saq_block_sparse_attn.
+ */
+int saq_block_sparse_attn_select(const void* q, const void* k, const void* v, const void* workspace,
+                                 size_t workspace_bytes, int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
+                                 double keep_ratio, float softmax_scale, void* o, uint8_t* block_mask_out,
+                                 void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* saq_status_string(int status);
 

@@ -23,7 +23,7 @@ from ._binding import SaqError, check, lib
 
 __all__ = ["qknorm_rope", "qknorm_rope_out", "qknorm_rope_pool", "select_blocks", "select_blocks_pooled",
            "select_workspace_bytes", "block_sparse_attn", "kept_blocks", "mask_overlap", "pooled_change", "pooled_bytes",
-           "MaskReuse", "quantize", "dequantize", "SaqError", "lib"]
+           "MaskReuse", "quantize", "dequantize", "block_sparse_attn_select", "SaqError", "lib"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -281,4 +281,30 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: str, block: int =
     fn = lib().saq_dequantize_int8 if fmt == "int8" else lib().saq_dequantize_fp8
     check(fn(codes.data_ptr(), scales.data_ptr(), B, S, H, D, block, out.data_ptr(), _stream(codes)),
           f"saq_dequantize_{fmt}")
+    return out
+
+
+def block_sparse_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor,
+                             keep_ratio: float, block: int = 128, scale: float = 0.0,
+                             out: Optional[torch.Tensor] = None, mask_out: Optional[torch.Tensor] = None):
+    """Attention with the block selection folded in, from the pooled means qknorm_rope_pool left in `workspace`
+    (saq_block_sparse_attn_select). Returns o; if `mask_out` (uint8 [B,H,nB,nB]) is given, the chosen rows are
+    written into it."""
+    _check_qkv("q", q)
+    _check_qkv("k", k, q)
+    _check_qkv("v", v, q)
+    B, S, H, D = q.shape
+    nB = -(-S // block)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv("out", out, q)
+    mptr = None
+    if mask_out is not None:
+        if mask_out.dtype != torch.uint8 or tuple(mask_out.shape) != (B, H, nB, nB) or not mask_out.is_contiguous():
+            raise ValueError("mask_out must be a contiguous uint8 [B,H,nB,nB] tensor")
+        mptr = mask_out.data_ptr()
+    st = lib().saq_block_sparse_attn_select(q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(), B, S, H, D, block,
+                                            float(keep_ratio), float(scale), out.data_ptr(), mptr, _stream(q))
+    check(st, "saq_block_sparse_attn_select")
     return out

@@ -48,6 +48,8 @@ SIGNATURES = [
     ("saq_dequantize_int8", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     ("saq_quantize_fp8", ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     ("saq_dequantize_fp8", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    ("saq_block_sparse_attn_select", ctypes.c_int, [_vp, _vp, _vp, _vp, _sz, _i32, _i32, _i32, _i32, _i32, _f64,
+                                                    _f32, _vp, _vp, _vp]),
     ("saq_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("saq_last_hip_error", ctypes.c_int, []),
 ]

@@ -427,10 +427,96 @@ __device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* 
     }
 }
 
+// In-kernel block selection (the selection folded into the attention pass):
+// the pooled fp64 block means of q-hat and k-hat, the number of kept blocks per
+// row, and an optional mask to write the chosen row into.
+struct SelectArgs {
+    const double* pq;        // [B][H][nB][D]
+    const double* pk;        // [B][H][nB][D]
+    int32_t kept;            // k: kept key blocks per query block, the diagonal included
+    uint8_t* mask_out;       // [B][H][nB][nB] or null
+};
+
+__device__ __forceinline__ uint64_t score_order_key(double s) {
+    uint64_t u = __double_as_longlong(s);
+    if (u == 0x8000000000000000ull) u = 0;                      // -0.0 ranks as +0.0
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Selects the kept key blocks of query block i of head bh into kept[0 .. n): the
+// diagonal plus the k-1 largest scores s_ij = sum_d pq_i[d] * pk_j[d] over j != i
+// (fp64, d ascending, each product and sum rounded: the selection's canonical
+// order), ties to the lower j; the same rule, order and result as the separate
+// score and top-k kernels. keys: kMaxBlocks uint64 of LDS scratch. The caller
+// synchronises the workgroup before reading kept / n_kept.
+__device__ __forceinline__ void select_row(const SelectArgs& a, int64_t bh, int i, int nB, uint64_t* keys,
+                                           uint16_t* kept, int* n_kept) {
+#pragma clang fp contract(off)
+    const double* pqi = a.pq + (bh * nB + i) * kD;
+    const double* pkh = a.pk + bh * nB * (int64_t)kD;
+    for (int j = threadIdx.x; j < nB; j += kThreads) {
+        const double2* pkj = (const double2*)(pkh + (int64_t)j * kD);
+        double s = 0.0;
+#pragma unroll 8
+        for (int d2 = 0; d2 < kD / 2; ++d2) {
+            const double2 y = pkj[d2];
+            const double p0 = pqi[2 * d2] * y.x;
+            s = s + p0;
+            const double p1 = pqi[2 * d2 + 1] * y.y;
+            s = s + p1;
+        }
+        keys[j] = score_order_key(s);
+    }
+    __syncthreads();
+    if (threadIdx.x >= kWave) return;
+    const int lane = threadIdx.x;
+    const int need = a.kept - 1;                        // blocks chosen besides the diagonal
+    uint64_t T = ~0ull;                                 // need == 0: nothing passes key > T
+    int eq_take = 0;
+    if (need > 0) {
+        // largest T with #(valid keys >= T) >= need, bit by bit from the top
+        T = 0;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t cand = T | (1ull << bit);
+            int cnt = 0;
+            for (int j0 = 0; j0 < nB; j0 += kWave) {
+                const int j = j0 + lane;
+                cnt += __popcll(__ballot(j < nB && j != i && keys[j] >= cand));
+            }
+            if (cnt >= need) T = cand;
+        }
+        int gt = 0;
+        for (int j0 = 0; j0 < nB; j0 += kWave) {
+            const int j = j0 + lane;
+            gt += __popcll(__ballot(j < nB && j != i && keys[j] > T));
+        }
+        eq_take = need - gt;
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint8_t* mrow = a.mask_out ? a.mask_out + (bh * nB + i) * (int64_t)nB : nullptr;
+    int taken = 0, count = 0;
+    for (int j0 = 0; j0 < nB; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool valid = j < nB && j != i;
+        const uint64_t key = j < nB ? keys[j] : 0;
+        const uint64_t eq = __ballot(valid && key == T);
+        const int before = taken + __popcll(eq & below);
+        const bool chosen = valid && (key > T || (key == T && before < eq_take));
+        taken += __popcll(eq);
+        const bool keep = chosen || j == i;
+        if (mrow && j < nB) mrow[j] = keep ? 1 : 0;
+        const uint64_t bits = __ballot(keep);
+        if (keep) kept[count + __popcll(bits & below)] = (uint16_t)j;
+        count += __popcll(bits);
+    }
+    if (lane == 0) *n_kept = count;
+}
+
+template <bool kSelect>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint8_t* __restrict__ mask, uint16_t* __restrict__ o, int32_t S, int32_t H, int32_t nB,
-    int64_t n_items, float scale_log2, uint32_t head_bytes) {
+    int64_t n_items, float scale_log2, uint32_t head_bytes, SelectArgs sel) {
     __shared__ __attribute__((aligned(1024))) uint8_t k_lds[kTileBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t v_lds[kTileBytes];
     __shared__ uint16_t kept[kMaxBlocks];
@@ -455,7 +541,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     const int l32 = lane % 32;
     const int g = lane / 32;
 
-    if (wave == 0) {
+    if constexpr (kSelect) {
+        // the K tile's LDS is free until the tile loop: it holds the row's score keys
+        select_row(sel, bh, i, nB, (uint64_t*)k_lds, kept, &n_kept_s);
+    } else if (wave == 0) {
         const uint8_t* mrow = mask + item * (int64_t)nB;
         int count = 0;
         for (int j0 = 0; j0 < nB; j0 += kWave) {
@@ -513,8 +602,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     }
 }
 
-hipError_t launch(const void* q, const void* k, const void* v, const uint8_t* mask, int32_t B, int32_t S, int32_t H,
-                  float scale, void* o, hipStream_t stream) {
+template <bool kSelect>
+hipError_t launch_t(const void* q, const void* k, const void* v, const uint8_t* mask, int32_t B, int32_t S, int32_t H,
+                    float scale, void* o, const SelectArgs& sel, hipStream_t stream) {
     const int32_t nB = (S + kBlock - 1) / kBlock;
     const int64_t n_items = (int64_t)B * H * nB;
     const int per = (nB + kNumXcd - 1) / kNumXcd;
@@ -522,10 +612,15 @@ hipError_t launch(const void* q, const void* k, const void* v, const uint8_t* ma
     const float scale_log2 = scale * 1.4426950408889634f;
     // bytes of one head's rows within one batch entry, up to the end of row S-1
     const uint64_t head_bytes = ((uint64_t)(S - 1) * H * kD + kD) * 2;
-    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)n_groups), dim3(kThreads), 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, mask, (uint16_t*)o, S, H, nB, n_items, scale_log2,
-                       (uint32_t)head_bytes);
+    hipLaunchKernelGGL(attn_kernel<kSelect>, dim3((unsigned)n_groups), dim3(kThreads), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, mask, (uint16_t*)o, S, H, nB,
+                       n_items, scale_log2, (uint32_t)head_bytes, sel);
     return hipGetLastError();
+}
+
+hipError_t launch(const void* q, const void* k, const void* v, const uint8_t* mask, int32_t B, int32_t S, int32_t H,
+                  float scale, void* o, hipStream_t stream) {
+    return launch_t<false>(q, k, v, mask, B, S, H, scale, o, SelectArgs{nullptr, nullptr, 0, nullptr}, stream);
 }
 
 }  // namespace d128
@@ -544,6 +639,14 @@ hipError_t launch_impl(const void* q, const void* k, const void* v, const uint8_
 }
 
 }  // namespace
+
+hipError_t launch_block_sparse_attn_select(const void* q, const void* k, const void* v, const double* pooled,
+                                           int32_t B, int32_t S, int32_t H, int32_t kept, float scale, void* o,
+                                           uint8_t* mask_out, hipStream_t stream) {
+    const int64_t nB = (S + d128::kBlock - 1) / d128::kBlock;
+    const d128::SelectArgs sel{pooled, pooled + (int64_t)B * H * nB * d128::kD, kept, mask_out};
+    return d128::launch_t<true>(q, k, v, nullptr, B, S, H, scale, o, sel, stream);
+}
 
 hipError_t launch_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* mask,
                                     int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,

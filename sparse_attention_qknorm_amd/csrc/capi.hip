@@ -342,6 +342,42 @@ int saq_block_sparse_attn(const void* q, const void* k, const void* v, const uin
                                                 (hipStream_t)stream));
 }
 
+int saq_block_sparse_attn_select(const void* q, const void* k, const void* v, const void* workspace,
+                                 size_t workspace_bytes, int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
+                                 double keep_ratio, float softmax_scale, void* o, uint8_t* block_mask_out,
+                                 void* stream) {
+    if (!q || !k || !v || !workspace || !o) return SAQ_ERR_NULL;
+    int st = check_dims(B, S, H, D);
+    if (st) return st;
+    st = check_block(S, block);
+    if (st) return st;
+    if (D != 128 || block != 128) return SAQ_ERR_UNSUPPORTED;
+    if (!isfinite(softmax_scale)) return SAQ_ERR_RANGE;
+    const int32_t nB = (S + block - 1) / block;
+    const int32_t kept = saq_kept_blocks(keep_ratio, nB);
+    if (kept < 0) return kept;
+    if ((int64_t)B * H * nB >= ((int64_t)1 << 31)) return SAQ_ERR_SHAPE;
+    const size_t pooled = (size_t)2 * B * H * nB * D * sizeof(double);
+    if (workspace_bytes < pooled) return SAQ_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAQ_ERR_ALIGN;
+    if (((uintptr_t)workspace & 255u) != 0) return SAQ_ERR_ALIGN;
+    const size_t bytes = (size_t)B * S * H * D * 2;
+    const size_t mbytes = (size_t)B * H * nB * nB;
+    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||
+        overlaps(o, bytes, workspace, pooled))
+        return SAQ_ERR_ALIAS;
+    if (block_mask_out &&
+        (overlaps(block_mask_out, mbytes, o, bytes) || overlaps(block_mask_out, mbytes, workspace, pooled) ||
+         overlaps(block_mask_out, mbytes, q, bytes) || overlaps(block_mask_out, mbytes, k, bytes) ||
+         overlaps(block_mask_out, mbytes, v, bytes)))
+        return SAQ_ERR_ALIAS;
+    st = device_ready();
+    if (st) return st;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+    return finish(saq::launch_block_sparse_attn_select(q, k, v, (const double*)workspace, B, S, H, kept, scale, o,
+                                                       block_mask_out, (hipStream_t)stream));
+}
+
 const char* saq_status_string(int status) {
     switch (status) {
         case SAQ_OK: return "ok";

@@ -88,3 +88,15 @@ hipError_t launch_dequantize(bool fp8, const void* codes, const float* scales, v
                              int32_t H, int32_t D, int32_t block, hipStream_t stream);
 
 }  // namespace saq
+
+namespace saq {
+
+// Attention with the block selection folded in (block 128, head_dim 128 only):
+// each workgroup selects its query block's kept key blocks from the pooled means
+// (pooled = the head of a workspace written by launch_qknorm_rope_pool) with the
+// selection's rule, optionally writes that mask row, and attends over them.
+hipError_t launch_block_sparse_attn_select(const void* q, const void* k, const void* v, const double* pooled,
+                                           int32_t B, int32_t S, int32_t H, int32_t kept, float scale, void* o,
+                                           uint8_t* mask_out, hipStream_t stream);
+
+}  // namespace saq

@@ -217,3 +217,20 @@ def test_codec_validation():
             assert f(x=x + 8) == -4 and f(codes=codes + 4) == -4 and f(scales=scales + 2) == -4
             assert f(codes=x + 1024) == -9                 # codes inside x
             assert f(scales=codes + 64) == -9              # scales inside codes
+
+
+def test_attn_select_validation():
+    lib = _binding.lib()
+    # S=1024, H=2, D=128: tensors 512 KiB each; pooled 2*2*8*128*8 = 32 KiB
+    q, k, v, o, ws = 1 << 24, 2 << 24, 3 << 24, 4 << 24, 5 << 24
+
+    def call(q=q, ws=ws, wbytes=1 << 20, D=128, block=128, keep=0.5, scale=0.0, o=o, mask=None):
+        return lib.saq_block_sparse_attn_select(q, k, v, ws, wbytes, 1, 1024, 2, D, block, keep, scale, o, mask, None)
+
+    assert call(q=None) == -1 and call(ws=None) == -1 and call(o=None) == -1
+    assert call(D=64, block=64) == -3 and call(block=64) == -3
+    assert call(keep=0.0) == -5 and call(scale=float("inf")) == -5
+    assert call(wbytes=32767) == -6
+    assert call(ws=ws + 16) == -4 and call(o=o + 8) == -4
+    assert call(o=q + 1024) == -9
+    assert call(mask=ws + 1024) == -9                  # mask inside the pooled means

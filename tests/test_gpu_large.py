@@ -246,3 +246,21 @@ def test_full_sweep_reuse(full):
         torch.cuda.synchronize()
         assert reuse.recomputed() != kept
         assert torch.equal(m, masks[0] if kept else masks[1])
+
+
+@pytest.mark.timeout(300)
+def test_full_folded_selection_matches_two_calls(full):
+    # the attention with the selection folded in gives the same mask and output bytes at the full size
+    c = full.cfg
+    keep = c.keep_ratios[0]
+    g = {n: full.inp[n].to(DEV) for n in ("q", "k", "pos_thw", "w_q", "w_k")}
+    qf, kf = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+    ws = saq.qknorm_rope_pool(g["q"], g["k"], qf, kf, g["pos_thw"], (g["w_q"], g["w_k"]), c.sections, c.rope_base,
+                              c.eps, c.block)
+    m2 = saq.select_blocks_pooled(qf.shape, keep, ws, c.block)
+    o2 = saq.block_sparse_attn(qf, kf, full.v, m2, c.block)
+    m1 = torch.empty_like(m2)
+    o1 = saq.block_sparse_attn_select(qf, kf, full.v, ws, keep, c.block, mask_out=m1)
+    torch.cuda.synchronize()
+    assert torch.equal(m1, m2) and torch.equal(o1, o2)
+    log("  full: attention with the folded selection bit-identical to select + attention (mask and output)")
