@@ -16,8 +16,8 @@
 //             fp64 and the result does not depend on the reduction order.
 //             HBM-bound: 4*D bytes per (token, head).
 //  2. scores: per (b, h) a tiled nB x nB product of the pooled vectors in fp64
-//             vector ALU (64x64 tile per workgroup, 4x4 per thread, pooled
-//             vectors staged in LDS by 32-wide d slices). Contraction into FMA
+//             vector ALU (128x128 tile per workgroup, 8x8 per thread, pooled
+//             vectors staged in LDS by 16-wide d slices). Contraction into FMA
 //             is switched off so every product and sum rounds on its own, in
 //             the same order as the definition. The scores leave as uint64
 //             keys whose unsigned order is the fp64 order (-0.0 -> +0.0).
@@ -86,22 +86,30 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const uint4* __restrict_
 
 // ---------------------------------------------------------------- scores
 
-constexpr int kTile = 64;      // scores per tile side
-constexpr int kSlice = 32;     // d values staged per pass
-
 __device__ __forceinline__ uint64_t order_key(double s) {
     uint64_t u = __double_as_longlong(s);
     if (u == 0x8000000000000000ull) u = 0;                      // -0.0 ranks as +0.0
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// 128 x 128 tiles, 8 x 8 scores per thread (rows ty + 16r, columns tx + 16s, so a
+// wavefront's column reads are 16 consecutive doubles and its row reads are
+// broadcasts), d staged 16 at a time into LDS rows padded to 129 doubles (the
+// transposing writes then spread over the banks) while the next 16 are loaded
+// into registers. Each score is sum over d ascending of the rounded products,
+// each partial sum rounded: the canonical order of the selection rule.
+constexpr int kTile2 = 128;
+constexpr int kSlice2 = 16;
+constexpr int kPad2 = kTile2 + 1;
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void scores_kernel(const double* __restrict__ pq, const double* __restrict__ pk,
-                                                          uint64_t* __restrict__ keys, int32_t nB, int32_t tiles,
-                                                          const double* __restrict__ gate) {
+__global__ __launch_bounds__(kThreads) void scores128_kernel(const double* __restrict__ pq,
+                                                             const double* __restrict__ pk,
+                                                             uint64_t* __restrict__ keys, int32_t nB, int32_t tiles,
+                                                             const double* __restrict__ gate) {
 #pragma clang fp contract(off)
-    __shared__ double sq[kSlice][kTile];
-    __shared__ double sk[kSlice][kTile];
+    __shared__ double sq[kSlice2][kPad2];
+    __shared__ double sk[kSlice2][kPad2];
     if (gate != nullptr && *gate == 0.0) return;        // the mask of an earlier step is kept
 
     const int64_t bh = blockIdx.x / ((int64_t)tiles * tiles);
@@ -113,34 +121,49 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const double* __restri
 
     const int tx = threadIdx.x % 16;
     const int ty = threadIdx.x / 16;
-    double acc[4][4];
+    double acc[8][8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 8; ++r)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc[r][s] = 0.0;
+        for (int s = 0; s < 8; ++s) acc[r][s] = 0.0;
 
-    for (int d0 = 0; d0 < D; d0 += kSlice) {
-        // stage pq[ti*64 .. +63][d0 .. d0+31] and pk likewise, transposed to [d][row]
-        for (int e = threadIdx.x; e < kSlice * kTile; e += kThreads) {
-            const int row = e / kSlice;
-            const int dd = e % kSlice;
-            const int gi = ti * kTile + row;
-            const int gj = tj * kTile + row;
-            sq[dd][row] = gi < nB ? a[(int64_t)gi * D + d0 + dd] : 0.0;
-            sk[dd][row] = gj < nB ? c[(int64_t)gj * D + d0 + dd] : 0.0;
+    // staging: element e = threadIdx.x + kThreads * m of a slice is (row e / kSlice2, d e % kSlice2); the
+    // next slice is loaded into registers while the current one is multiplied
+    constexpr int kPer = kSlice2 * kTile2 / kThreads;
+    double nq[kPer], nk[kPer];
+    auto fetch = [&](int d0) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int e = threadIdx.x + kThreads * m;
+            const int row = e / kSlice2;
+            const int dd = e % kSlice2;
+            const int gi = ti * kTile2 + row;
+            const int gj = tj * kTile2 + row;
+            nq[m] = gi < nB ? a[(int64_t)gi * D + d0 + dd] : 0.0;
+            nk[m] = gj < nB ? c[(int64_t)gj * D + d0 + dd] : 0.0;
+        }
+    };
+    fetch(0);
+    for (int d0 = 0; d0 < D; d0 += kSlice2) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int e = threadIdx.x + kThreads * m;
+            sq[e % kSlice2][e / kSlice2] = nq[m];
+            sk[e % kSlice2][e / kSlice2] = nk[m];
         }
         __syncthreads();
-#pragma unroll 4
-        for (int dd = 0; dd < kSlice; ++dd) {
-            double x[4], y[4];
+        if (d0 + kSlice2 < D) fetch(d0 + kSlice2);
+#pragma unroll 2
+        for (int dd = 0; dd < kSlice2; ++dd) {
+            double x[8], y[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = sq[dd][ty * 4 + r];
+            for (int r = 0; r < 8; ++r) x[r] = sq[dd][ty + 16 * r];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) y[s] = sk[dd][tx * 4 + s];
+            for (int s = 0; s < 8; ++s) y[s] = sk[dd][tx + 16 * s];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 8; ++r)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
+                for (int s = 0; s < 8; ++s) {
                     const double prod = x[r] * y[s];
                     acc[r][s] = acc[r][s] + prod;
                 }
@@ -149,12 +172,12 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(const double* __restri
     }
     uint64_t* out = keys + bh * (int64_t)nB * nB;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int gi = ti * kTile + ty * 4 + r;
+    for (int r = 0; r < 8; ++r) {
+        const int gi = ti * kTile2 + ty + 16 * r;
         if (gi >= nB) continue;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int gj = tj * kTile + tx * 4 + s;
+        for (int s = 0; s < 8; ++s) {
+            const int gj = tj * kTile2 + tx + 16 * s;
             if (gj < nB) out[(int64_t)gi * nB + gj] = order_key(acc[r][s]);
         }
     }
@@ -241,13 +264,13 @@ hipError_t launch_select_from_pooled(int32_t B, int32_t S, int32_t H, int32_t D,
     const size_t pooled_bytes = ((size_t)2 * B * H * nB * D * sizeof(double) + 255) / 256 * 256;
     uint64_t* keys = (uint64_t*)((char*)workspace + pooled_bytes);
 
-    const int32_t tiles = (nB + kTile - 1) / kTile;
+    const int32_t tiles = (nB + kTile2 - 1) / kTile2;
     const dim3 score_grid((unsigned)((int64_t)B * H * tiles * tiles));
     if (D == 128) {
-        hipLaunchKernelGGL((scores_kernel<128>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles,
+        hipLaunchKernelGGL((scores128_kernel<128>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles,
                            gate);
     } else {
-        hipLaunchKernelGGL((scores_kernel<64>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles,
+        hipLaunchKernelGGL((scores128_kernel<64>), score_grid, dim3(kThreads), 0, stream, pq, pk, keys, nB, tiles,
                            gate);
     }
     hipError_t err = hipGetLastError();
