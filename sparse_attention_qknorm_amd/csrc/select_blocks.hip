@@ -22,8 +22,9 @@
 //             the same order as the definition. The scores leave as uint64
 //             keys whose unsigned order is the fp64 order (-0.0 -> +0.0).
 //  3. topk:   one wavefront per query-block row; the row's keys sit in
-//             registers; a 64-step bitwise search over the key value, counting
-//             with wave ballots, finds the (k-1)-th largest key T; keys > T are
+//             registers; a bitwise search over the key value, counting with
+//             wave ballots, finds the (k-1)-th largest key T (32 steps on the
+//             upper halves, 32 more only when keys tie there); keys > T are
 //             kept, and keys == T are kept in ascending j until k-1 are kept.
 #include "common.h"
 #include "kernels.h"
@@ -214,18 +215,41 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const uint64_t* __restri
     uint64_t T = ~0ull;                                   // need == 0: nothing passes key > T
     int eq_take = 0;
     if (need > 0) {
-        T = 0;
-        for (int bit = 63; bit >= 0; --bit) {
-            const uint64_t cand = T | (1ull << bit);
+        // The search runs on the upper 32 bits first. When every key whose upper half equals the
+        // threshold's is kept anyway (the common case: distinct scores rarely agree in their top
+        // 32 bits), the selection is already decided; otherwise the search goes on through the
+        // lower 32 bits exactly as a 64-step search would.
+        uint32_t T32 = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T32 | (1u << bit);
             int cnt = 0;
 #pragma unroll
-            for (int r = 0; r < R; ++r) cnt += wave_count(valid[r] && key[r] >= cand);
-            if (cnt >= need) T = cand;
+            for (int r = 0; r < R; ++r) cnt += wave_count(valid[r] && (uint32_t)(key[r] >> 32) >= cand);
+            if (cnt >= need) T32 = cand;
         }
-        int gt = 0;
+        int gt32 = 0, eq32 = 0;
 #pragma unroll
-        for (int r = 0; r < R; ++r) gt += wave_count(valid[r] && key[r] > T);
-        eq_take = need - gt;
+        for (int r = 0; r < R; ++r) {
+            const uint32_t hi = (uint32_t)(key[r] >> 32);
+            gt32 += wave_count(valid[r] && hi > T32);
+            eq32 += wave_count(valid[r] && hi == T32);
+        }
+        if (T32 != 0 && need - gt32 == eq32) {
+            T = ((uint64_t)T32 << 32) - 1ull;             // keys > T: exactly those with upper half >= T32
+        } else {
+            T = (uint64_t)T32 << 32;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint64_t cand = T | (1ull << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) cnt += wave_count(valid[r] && key[r] >= cand);
+                if (cnt >= need) T = cand;
+            }
+            int gt = 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) gt += wave_count(valid[r] && key[r] > T);
+            eq_take = need - gt;
+        }
     }
     const uint64_t below = (1ull << lane) - 1ull;         // lanes with a lower j in this group
     int taken = 0;
