@@ -373,8 +373,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer would shard by "
-              "heads; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the layer would shard by "
+              "heads across GPUs, with an all-to-all on either side of the attention). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     if args.workload == "codecs":

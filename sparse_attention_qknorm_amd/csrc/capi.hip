@@ -21,8 +21,14 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 int check_dims(int32_t B, int32_t S, int32_t H, int32_t D) {
     if (B < 1 || S < 1 || H < 1 || D < 1) return SAQ_ERR_SHAPE;
     if (D != 64 && D != 128) return SAQ_ERR_UNSUPPORTED;
-    const int64_t n = (int64_t)B * S * H * D;
-    if (n >= ((int64_t)1 << 31)) return SAQ_ERR_SHAPE;
+    // B*S*H*D < 2^31, checked factor by factor so that no product can overflow
+    const int64_t lim = (int64_t)1 << 31;
+    int64_t n = (int64_t)B * S;
+    if (n >= lim) return SAQ_ERR_SHAPE;
+    n *= H;
+    if (n >= lim) return SAQ_ERR_SHAPE;
+    n *= D;
+    if (n >= lim) return SAQ_ERR_SHAPE;
     return SAQ_OK;
 }
 
@@ -57,7 +63,7 @@ int validate_prologue(const void* q_in, const void* k_in, const void* q_out, con
     if (!q_in || !k_in || !q_out || !k_out || !pos_thw || !w_q || !w_k) return SAQ_ERR_NULL;
     int st = check_dims(B, S, H, D);
     if (st) return st;
-    if (dt < 0 || dh < 0 || dw < 0 || dt + dh + dw != D || (dt | dh | dw) & 1) return SAQ_ERR_SHAPE;
+    if (dt < 0 || dh < 0 || dw < 0 || (int64_t)dt + dh + dw != D || (dt | dh | dw) & 1) return SAQ_ERR_SHAPE;
     if (!(base > 1.0) || !isfinite(base) || !(eps > 0.0) || !isfinite(eps)) return SAQ_ERR_RANGE;
     if (!aligned16(q_in) || !aligned16(k_in) || !aligned16(q_out) || !aligned16(k_out)) return SAQ_ERR_ALIGN;
     const size_t bytes = (size_t)B * S * H * D * 2;
