@@ -114,6 +114,13 @@ size_t saq_select_blocks_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_
  *      equals +0.0.
  * Output: block_mask [B,H,nB,nB] uint8 with exactly k ones per row and a one
  * on the diagonal. Bit-for-bit deterministic. Inputs must be finite.
+ * The block sums of step 1 are exact, hence independent of summation order
+ * (and equal between this call and saq_qknorm_rope_pool), when every value
+ * satisfies |x| < 16 and is 0 or >= 2^-35 in magnitude. QKNorm output with
+ * weights of magnitude < 1.4 meets the upper bound for D <= 128 (|x_hat| <=
+ * sqrt(D) * max|w|); the lower one fails only for values that tiny. Outside
+ * that range the result is still deterministic, but the two selection paths
+ * may round the means differently.
  *
  *   q, k       bf16 [B,S,H,D]: the post-prologue tensors attention consumes.
  *   workspace  device buffer of at least
