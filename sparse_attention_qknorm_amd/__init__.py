@@ -9,6 +9,13 @@ Three calls, each a thin wrapper over the C ABI of libsaq.so (include/saq.h):
     mask = select_blocks(q, k, keep_ratio, block)                 # uint8 [B,H,nB,nB]
     o = block_sparse_attn(q, k, v, mask, block)                   # bf16 [B,S,H,D]
 
+Also: ``attention_layer`` (the three steps with the pooling fused into the
+prologue), ``qknorm_rope_pool`` + ``select_blocks_pooled`` (that fused form
+call by call), ``block_sparse_attn_select`` (selection inside the attention
+kernel), ``MaskReuse`` / ``mask_overlap`` / ``pooled_change`` (cross-step mask
+reuse and its measurements), ``quantize`` / ``dequantize`` (INT8 / FP8 block
+codecs).
+
 Tensors live on a ROCm device; torch provides memory and the current stream
 only. The library must be built (``python -m sparse_attention_qknorm_amd.build``);
 without it every call raises.
@@ -23,7 +30,8 @@ from ._binding import SaqError, check, lib
 
 __all__ = ["qknorm_rope", "qknorm_rope_out", "qknorm_rope_pool", "select_blocks", "select_blocks_pooled",
            "select_workspace_bytes", "block_sparse_attn", "kept_blocks", "mask_overlap", "pooled_change", "pooled_bytes",
-           "MaskReuse", "quantize", "dequantize", "block_sparse_attn_select", "SaqError", "lib"]
+           "MaskReuse", "quantize", "dequantize", "block_sparse_attn_select", "attention_layer",
+           "SaqError", "lib"]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -308,3 +316,27 @@ def block_sparse_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                                             float(keep_ratio), float(scale), out.data_ptr(), mptr, _stream(q))
     check(st, "saq_block_sparse_attn_select")
     return out
+
+
+def attention_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pos_thw: torch.Tensor,
+                    weights: Tuple[torch.Tensor, torch.Tensor], sections: Sequence[int], keep_ratio: float,
+                    block: int = 128, base: float = 10000.0, eps: float = 1e-6, scale: float = 0.0,
+                    buffers: Optional[dict] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The whole layer in three library calls: fused QKNorm + 3D RoPE with block pooling, selection from the
+    pooled means, block-sparse attention. q and k are not modified. Returns (o, block_mask).
+
+    `buffers` (optional dict) keeps device buffers across calls of the same shape: keys "q_hat", "k_hat",
+    "workspace", "mask", "o" are filled on first use and reused afterwards."""
+    B, S, H, D = q.shape
+    nB = -(-S // block)
+    buf = {} if buffers is None else buffers
+    if "q_hat" not in buf:
+        buf["q_hat"], buf["k_hat"] = torch.empty_like(q), torch.empty_like(k)
+        buf["workspace"] = torch.empty(select_workspace_bytes(B, S, H, D, block), dtype=torch.uint8, device=q.device)
+        buf["mask"] = torch.empty((B, H, nB, nB), dtype=torch.uint8, device=q.device)
+        buf["o"] = torch.empty_like(q)
+    qknorm_rope_pool(q, k, buf["q_hat"], buf["k_hat"], pos_thw, weights, sections, base, eps, block,
+                     workspace=buf["workspace"])
+    select_blocks_pooled(q.shape, keep_ratio, buf["workspace"], block, out=buf["mask"])
+    block_sparse_attn(buf["q_hat"], buf["k_hat"], v, buf["mask"], block, scale, out=buf["o"])
+    return buf["o"], buf["mask"]

@@ -88,3 +88,28 @@ def test_fused_rejects_too_many_channels():
     pos = torch.zeros((8, 3), dtype=torch.int32, device=DEV)
     with pytest.raises(saq.SaqError):
         saq.qknorm_rope_pool(q, q.clone(), torch.empty_like(q), torch.empty_like(q), pos, (w, w), (32, 48, 48))
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_attention_layer_entry(name):
+    # the one-call layer equals the step-by-step calls byte for byte, reuses its buffers, and leaves q, k alone
+    cfg = synth.get_config(name)
+    inp = synth.make_inputs(cfg)
+    g = {n: inp[n].to(DEV) for n in ("q", "k", "v", "pos_thw", "w_q", "w_k")}
+    q0, k0 = g["q"].clone(), g["k"].clone()
+    keep = cfg.keep_ratios[0]
+    bufs = {}
+    o1, m1 = saq.attention_layer(g["q"], g["k"], g["v"], g["pos_thw"], (g["w_q"], g["w_k"]), cfg.sections, keep,
+                                 cfg.block, cfg.rope_base, cfg.eps, buffers=bufs)
+    o1, m1 = o1.clone(), m1.clone()
+    o2, m2 = saq.attention_layer(g["q"], g["k"], g["v"], g["pos_thw"], (g["w_q"], g["w_k"]), cfg.sections, keep,
+                                 cfg.block, cfg.rope_base, cfg.eps, buffers=bufs)
+    qs, ks = torch.empty_like(q0), torch.empty_like(k0)
+    saq.qknorm_rope_out(g["q"], g["k"], qs, ks, g["pos_thw"], (g["w_q"], g["w_k"]), cfg.sections, cfg.rope_base,
+                        cfg.eps)
+    ms = saq.select_blocks(qs, ks, keep, cfg.block)
+    os_ = saq.block_sparse_attn(qs, ks, g["v"], ms, cfg.block)
+    torch.cuda.synchronize()
+    assert torch.equal(g["q"], q0) and torch.equal(g["k"], k0)
+    assert torch.equal(o1, o2) and torch.equal(m1, m2) and o2.data_ptr() == bufs["o"].data_ptr()
+    assert torch.equal(m1, ms) and torch.equal(o1, os_)
