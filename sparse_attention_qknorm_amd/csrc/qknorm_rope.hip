@@ -132,56 +132,58 @@ namespace saq {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Fused form with block pooling. One workgroup per (b, block of `block` tokens,
-// group of kHeadGroup heads): 256 threads, each owning one 16-byte chunk position
-// (tensor, head, 8 channels) for the whole block. The workgroup walks the block's
-// tokens kTokStep at a time (that many loads in flight per thread), applies QKNorm
-// + RoPE as above, writes the bf16 results, and accumulates the rounded bf16 values
-// it wrote in fp64. Sums of bf16 values with |x| < 16 are exact in fp64, so the
-// means equal those of the separate pooling pass bit for bit, and the pass saves
-// that pass's re-read of q-hat and k-hat.
+// Fused form with block pooling. One workgroup per (b, block of `block` tokens)
+// covering every head: one thread per 16-byte chunk position (head, 8
+// channels) of a token row, H*D/8 of them (rounded up to whole wavefronts),
+// each handling that position of both q and k for the whole block. The
+// workgroup walks the block's tokens one at a time, applies QKNorm + RoPE
+// exactly as the per-token kernel above (same arithmetic, same bits), writes
+// the bf16 results, and accumulates the rounded bf16 values it wrote in fp64.
+// Sums of bf16 values with |x| < 16 are exact in fp64, so the means equal those
+// of the separate pooling pass bit for bit, and the pass saves that pass's
+// re-read of q-hat and k-hat. Each token's rotation angles are computed once
+// (fp64 sincos, staged in LDS kTokChunk tokens at a time) for all heads of q
+// and k. Measured at the full shape: one token per step and whole rows per
+// workgroup beat splitting the heads over workgroups or keeping more tokens in
+// flight per thread.
+constexpr int kPoolMaxThreads = 1024;                          // H*D <= 8192
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void qknorm_rope_pool_kernel(
+__global__ __launch_bounds__(kPoolMaxThreads) void qknorm_rope_pool_kernel(
     const uint4* q_in, const uint4* k_in, uint4* q_out, uint4* k_out, const int32_t* __restrict__ pos_thw,
     const float* __restrict__ w_q, const float* __restrict__ w_k, int32_t S, int32_t H, RopeTable table, float eps,
-    int32_t block, int32_t nB, int32_t n_groups, double* __restrict__ pooled) {
+    int32_t block, int32_t nB, double* __restrict__ pooled) {
     constexpr int kLanesPerRow = D / 8;
     constexpr int kPairs = D / 2;
-    constexpr int kHeadGroup = kThreads / 2 / kLanesPerRow;   // heads per workgroup (q and k)
     constexpr int kTokChunk = 32;                              // tokens whose angles are staged at once
-    constexpr int kTokStep = 2;                                // tokens loaded together (2 measured best: 1.32 ms
-                                                               // at the full shape against 1.41 for 4, 2.0 for 8)
     __shared__ float2 cs[kTokChunk][kPairs];
 
-    const int64_t id = blockIdx.x;                             // (b * nB + i) * n_groups + hg
-    const int hg = (int)(id % n_groups);
-    const int64_t bi = id / n_groups;
+    const int T = (int)blockDim.x;
+    const int64_t bi = blockIdx.x;                             // b * nB + i
     const int i = (int)(bi % nB);
     const int64_t b = bi / nB;
     const int t0 = i * block;
     const int t1 = min(t0 + block, S);
     const int tid = threadIdx.x;
-    const int tensor = tid / (kThreads / 2);                   // 0: q, 1: k
-    const int within = tid % (kThreads / 2);
-    const int h = hg * kHeadGroup + within / kLanesPerRow;
-    const int lane_in_row = within % kLanesPerRow;
-    const bool active = h < H;                                 // whole rows in or out together
-    const int64_t row_chunks = (int64_t)H * kLanesPerRow;      // 16-byte chunks per token per tensor
-    const uint4* src = tensor == 0 ? q_in : k_in;
-    uint4* dst = tensor == 0 ? q_out : k_out;
-    const float* wv = tensor == 0 ? w_q : w_k;
-    float w[8];
+    const int P = H * kLanesPerRow;                            // chunk positions per token row
+    const bool active = tid < P;                               // whole rows in or out together
+    const int lane_in_row = tid % kLanesPerRow;
+    float wq[8], wk[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = wv[lane_in_row * 8 + e];
-    double acc[8];
+    for (int e = 0; e < 8; ++e) {
+        wq[e] = w_q[lane_in_row * 8 + e];
+        wk[e] = w_k[lane_in_row * 8 + e];
+    }
+    double acc[2][8];                                          // [tensor][channel]
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    const int64_t col = (int64_t)h * kLanesPerRow + lane_in_row;
+    for (int ten = 0; ten < 2; ++ten)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[ten][e] = 0.0;
 
     for (int tc = t0; tc < t1; tc += kTokChunk) {
         const int nt = min(kTokChunk, t1 - tc);
         __syncthreads();                                       // previous chunk's angles consumed
-        for (int wi = tid; wi < nt * kPairs; wi += kThreads) {
+        for (int wi = tid; wi < nt * kPairs; wi += T) {
             const int tt = wi / kPairs, p = wi % kPairs;
             const int axis = p < table.pair_end_t ? 0 : (p < table.pair_end_h ? 1 : 2);
             const double theta = (double)pos_thw[(int64_t)(tc + tt) * 3 + axis] * table.inv_freq[p];
@@ -190,15 +192,16 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_pool_kernel(
             cs[tt][p] = make_float2((float)cn, (float)sn);
         }
         __syncthreads();
-        for (int ts = 0; ts < nt; ts += kTokStep) {
-            uint4 raw[kTokStep];
+        if (!active) continue;
+        for (int ts = 0; ts < nt; ++ts) {
+            const int64_t at = (b * S + tc + ts) * (int64_t)P + tid;
+            const uint4 raw[2] = {q_in[at], k_in[at]};
+            float2 rot[4];
 #pragma unroll
-            for (int u = 0; u < kTokStep; ++u)
-                if (active && ts + u < nt) raw[u] = src[(b * S + tc + ts + u) * row_chunks + col];
+            for (int p = 0; p < 4; ++p) rot[p] = cs[ts][lane_in_row * 4 + p];
 #pragma unroll
-            for (int u = 0; u < kTokStep; ++u) {
-                if (!(active && ts + u < nt)) continue;
-                const uint32_t w32[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+            for (int ten = 0; ten < 2; ++ten) {
+                const uint32_t w32[4] = {raw[ten].x, raw[ten].y, raw[ten].z, raw[ten].w};
                 float x[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -214,24 +217,28 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_pool_kernel(
                 uint32_t outw[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const float2 r = cs[ts + u][lane_in_row * 4 + p];
-                    const float y0 = x[2 * p] * rinv * w[2 * p];
-                    const float y1 = x[2 * p + 1] * rinv * w[2 * p + 1];
-                    const uint32_t h0 = f32_to_bf16_bits(y0 * r.x - y1 * r.y);
-                    const uint32_t h1 = f32_to_bf16_bits(y0 * r.y + y1 * r.x);
+                    const float y0 = x[2 * p] * rinv * (ten == 0 ? wq[2 * p] : wk[2 * p]);
+                    const float y1 = x[2 * p + 1] * rinv * (ten == 0 ? wq[2 * p + 1] : wk[2 * p + 1]);
+                    const uint32_t h0 = f32_to_bf16_bits(y0 * rot[p].x - y1 * rot[p].y);
+                    const uint32_t h1 = f32_to_bf16_bits(y0 * rot[p].y + y1 * rot[p].x);
                     outw[p] = h0 | (h1 << 16);
-                    acc[2 * p] += (double)bf16_bits_to_f32(h0);
-                    acc[2 * p + 1] += (double)bf16_bits_to_f32(h1);
+                    acc[ten][2 * p] += (double)bf16_bits_to_f32(h0);
+                    acc[ten][2 * p + 1] += (double)bf16_bits_to_f32(h1);
                 }
-                dst[(b * S + tc + ts + u) * row_chunks + col] = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+                const uint4 o = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+                if (ten == 0) q_out[at] = o;
+                else k_out[at] = o;
             }
         }
     }
-    if (active) {
-        const int64_t Bsz = gridDim.x / ((int64_t)nB * n_groups);
-        double* out = pooled + ((((int64_t)tensor * Bsz + b) * H + h) * nB + i) * (int64_t)D + lane_in_row * 8;
+    if (!active) return;
+    const int64_t Bsz = gridDim.x / nB;
+    const int h = tid / kLanesPerRow;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = acc[e] / (double)(t1 - t0);
+    for (int ten = 0; ten < 2; ++ten) {
+        double* out = pooled + ((((int64_t)ten * Bsz + b) * H + h) * nB + i) * (int64_t)D + lane_in_row * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = acc[ten][e] / (double)(t1 - t0);
     }
 }
 
@@ -239,11 +246,11 @@ template <int D>
 void launch_pool_d(const void* q_in, const void* k_in, void* q_out, void* k_out, const int32_t* pos_thw,
                    const float* w_q, const float* w_k, int32_t B, int32_t S, int32_t H, const RopeTable& table,
                    float eps, int32_t block, int32_t nB, double* pooled, hipStream_t stream) {
-    constexpr int kHeadGroup = kThreads / 2 / (D / 8);
-    const int32_t n_groups = (H + kHeadGroup - 1) / kHeadGroup;
-    hipLaunchKernelGGL((qknorm_rope_pool_kernel<D>), dim3((unsigned)((int64_t)B * nB * n_groups)), dim3(kThreads), 0,
-                       stream, (const uint4*)q_in, (const uint4*)k_in, (uint4*)q_out, (uint4*)k_out, pos_thw, w_q,
-                       w_k, S, H, table, eps, block, nB, n_groups, pooled);
+    const int P = H * (D / 8);                                 // <= kMaxRowElems / 8 = 1024
+    const int T = ((P + kWave - 1) / kWave) * kWave;
+    hipLaunchKernelGGL((qknorm_rope_pool_kernel<D>), dim3((unsigned)((int64_t)B * nB)), dim3(T), 0, stream,
+                       (const uint4*)q_in, (const uint4*)k_in, (uint4*)q_out, (uint4*)k_out, pos_thw, w_q, w_k, S,
+                       H, table, eps, block, nB, pooled);
 }
 
 }  // namespace
