@@ -61,14 +61,16 @@ def computed_flops(mask, S: int, block: int, D: int) -> float:
     return float(4.0 * D * torch.einsum("bhij,i,j->", m, n, n).item())
 
 
-def measured_traffic(kernel_hash: str, steps_launches: int):
-    """HBM bytes per attention launch from the committed counter runs, if they match this kernel."""
+def measured_traffic(kernel_hash: str, workload: str, keep: float, path: str):
+    """HBM bytes per attention launch from the committed counter runs, if they were taken on this kernel source,
+    this workload and keep ratio, and the attention kernel without the folded selection; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash:
+    if (rec.get("kernel_hash") != kernel_hash or rec.get("config") != workload or rec.get("keep_ratio") != keep
+            or path == "folded"):
         return None
     return rec.get("bytes_per_launch")
 
@@ -464,7 +466,7 @@ def main(argv=None) -> int:
     att_s = ms["att"] / 1e3
     achieved = flops / att_s / 1e12
     khash = attn_source_hash()
-    traffic = measured_traffic(khash, args.steps)
+    traffic = measured_traffic(khash, cfg.name, keep, args.path)
     pro_bytes = 8.0 * cfg.D * cfg.H * cfg.B * cfg.S + 12.0 * cfg.S
 
     result = {
