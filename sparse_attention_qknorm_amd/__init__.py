@@ -38,6 +38,14 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _check_buf(name: str, t: torch.Tensor, device: Optional[torch.device] = None) -> None:
+    """A buffer handed to the library: a contiguous device tensor (on `device` when given)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
 def _check_qkv(name: str, t: torch.Tensor, ref: Optional[torch.Tensor] = None) -> None:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -99,6 +107,7 @@ def qknorm_rope_pool(q: torch.Tensor, k: torch.Tensor, q_out: torch.Tensor, k_ou
     need = select_workspace_bytes(B, S, H, D, block)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_buf("workspace", workspace, q.device)
     dt, dh, dw = (int(x) for x in sections)
     w_q, w_k = weights
     st = lib().saq_qknorm_rope_pool(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
@@ -115,10 +124,12 @@ def select_blocks_pooled(shape: Sequence[int], keep_ratio: float, workspace: tor
     shape = (B, S, H, D) of q."""
     B, S, H, D = (int(x) for x in shape)
     nB = -(-S // block)
+    _check_buf("workspace", workspace)
     if out is None:
         out = torch.empty((B, H, nB, nB), dtype=torch.uint8, device=workspace.device)
     elif out.dtype != torch.uint8 or tuple(out.shape) != (B, H, nB, nB) or not out.is_contiguous():
         raise ValueError("out must be a contiguous uint8 [B,H,nB,nB] tensor")
+    _check_buf("out", out, workspace.device)
     st = lib().saq_select_blocks_pooled(B, S, H, D, block, float(keep_ratio), out.data_ptr(), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), _stream(workspace))
     check(st, "saq_select_blocks_pooled")
@@ -153,6 +164,8 @@ def select_blocks(q: torch.Tensor, k: torch.Tensor, keep_ratio: float, block: in
     need = select_workspace_bytes(B, S, H, D, block)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_buf("out", out, q.device)
+    _check_buf("workspace", workspace, q.device)
     st = lib().saq_select_blocks(q.data_ptr(), k.data_ptr(), B, S, H, D, block, float(keep_ratio), out.data_ptr(),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
     check(st, "saq_select_blocks")
@@ -169,6 +182,7 @@ def block_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_m
     nB = -(-S // block)
     if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (B, H, nB, nB) or not block_mask.is_contiguous():
         raise ValueError("block_mask must be a contiguous uint8 [B,H,nB,nB] tensor")
+    _check_buf("block_mask", block_mask, q.device)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -184,8 +198,8 @@ def mask_overlap(mask_a: torch.Tensor, mask_b: torch.Tensor) -> torch.Tensor:
     for n, m in (("mask_a", mask_a), ("mask_b", mask_b)):
         if m.dtype != torch.uint8 or m.dim() != 4 or not m.is_contiguous() or not m.is_cuda:
             raise ValueError(f"{n} must be a contiguous uint8 [B,H,nB,nB] device tensor")
-    if mask_a.shape != mask_b.shape:
-        raise ValueError("masks must have the same shape")
+    if mask_a.shape != mask_b.shape or mask_a.device != mask_b.device:
+        raise ValueError("masks must have the same shape and device")
     B, H, nB, _ = mask_a.shape
     counts = torch.empty((B, H, 2), dtype=torch.int64, device=mask_a.device)
     st = lib().saq_mask_overlap(mask_a.data_ptr(), mask_b.data_ptr(), B, H, nB, counts.data_ptr(), _stream(mask_a))
@@ -199,8 +213,13 @@ def pooled_change(ws_prev: torch.Tensor, ws_cur: torch.Tensor, shape: Sequence[i
     in two selection workspaces (saq_pooled_change). The relative change is sqrt([0] / [1])."""
     B, S, H, D = (int(x) for x in shape)
     n = lib().saq_pooled_change_out_len()
+    _check_buf("ws_cur", ws_cur)
+    _check_buf("ws_prev", ws_prev, ws_cur.device)
     if out is None:
         out = torch.empty(n, dtype=torch.float64, device=ws_cur.device)
+    if out.dtype != torch.float64:
+        raise ValueError("out must be a float64 tensor")
+    _check_buf("out", out, ws_cur.device)
     st = lib().saq_pooled_change(ws_prev.data_ptr(), ws_cur.data_ptr(), B, S, H, D, block, out.data_ptr(),
                                  out.numel(), _stream(ws_cur))
     check(st, "saq_pooled_change")
@@ -233,6 +252,7 @@ class MaskReuse:
 
     def step(self, workspace: torch.Tensor, force: bool = False) -> torch.Tensor:
         B, S, H, D = self.shape
+        _check_buf("workspace", workspace, self.mask.device)
         f = 1 if (force or not self.started) else 0
         st = lib().saq_select_blocks_reuse(B, S, H, D, self.block, self.keep_ratio, self.threshold, f,
                                            self.mask.data_ptr(), workspace.data_ptr(),
@@ -267,6 +287,8 @@ def quantize(x: torch.Tensor, fmt: str, block: int = 128, codes: Optional[torch.
         raise ValueError(f"codes must be a contiguous {cdt} [B,S,H,D] tensor")
     if scales.dtype != torch.float32 or tuple(scales.shape) != (B, H, nB) or not scales.is_contiguous():
         raise ValueError("scales must be a contiguous float32 [B,H,nB] tensor")
+    _check_buf("codes", codes, x.device)
+    _check_buf("scales", scales, x.device)
     fn = lib().saq_quantize_int8 if fmt == "int8" else lib().saq_quantize_fp8
     check(fn(x.data_ptr(), B, S, H, D, block, codes.data_ptr(), scales.data_ptr(), _stream(x)),
           f"saq_quantize_{fmt}")
@@ -283,9 +305,12 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, fmt: str, block: int =
     nB = -(-S // block)
     if scales.dtype != torch.float32 or tuple(scales.shape) != (B, H, nB) or not scales.is_contiguous():
         raise ValueError("scales must be a contiguous float32 [B,H,nB] tensor")
+    _check_buf("scales", scales, codes.device)
     if out is None:
         out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=codes.device)
     _check_qkv("out", out)
+    if out.shape != codes.shape or out.device != codes.device:
+        raise ValueError("out must match codes' shape and device")
     fn = lib().saq_dequantize_int8 if fmt == "int8" else lib().saq_dequantize_fp8
     check(fn(codes.data_ptr(), scales.data_ptr(), B, S, H, D, block, out.data_ptr(), _stream(codes)),
           f"saq_dequantize_{fmt}")
@@ -306,10 +331,12 @@ def block_sparse_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     if out is None:
         out = torch.empty_like(q)
     _check_qkv("out", out, q)
+    _check_buf("workspace", workspace, q.device)
     mptr = None
     if mask_out is not None:
         if mask_out.dtype != torch.uint8 or tuple(mask_out.shape) != (B, H, nB, nB) or not mask_out.is_contiguous():
             raise ValueError("mask_out must be a contiguous uint8 [B,H,nB,nB] tensor")
+        _check_buf("mask_out", mask_out, q.device)
         mptr = mask_out.data_ptr()
     st = lib().saq_block_sparse_attn_select(q.data_ptr(), k.data_ptr(), v.data_ptr(), workspace.data_ptr(),
                                             workspace.numel() * workspace.element_size(), B, S, H, D, block,

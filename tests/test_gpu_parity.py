@@ -151,3 +151,35 @@ def test_out_of_place_prologue_matches_in_place():
     saq.qknorm_rope_out(g["q"], g["k"], qo, ko, g["pos_thw"], (g["w_q"], g["w_k"]), cfg.sections)
     saq.qknorm_rope(g["q"], g["k"], g["pos_thw"], (g["w_q"], g["w_k"]), cfg.sections)
     assert torch.equal(qo, g["q"]) and torch.equal(ko, g["k"])
+
+
+def test_host_or_strided_buffers_rejected_before_launch():
+    # every buffer a wrapper hands to the library must be a contiguous tensor on the inputs' device: a host
+    # tensor or a strided view is refused with ValueError before any call into the library
+    inp = synth.make_small_case(256, 2, 64, seed=5, sections=(16, 24, 24), T=0)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    B, S, H, D = q.shape
+    nB = S // 64
+    mask = saq.select_blocks(q, k, 0.5, 64)
+    ws = torch.empty(saq.select_workspace_bytes(B, S, H, D, 64), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    cases = {
+        "block_sparse_attn mask on host": lambda: saq.block_sparse_attn(q, k, v, mask.cpu(), 64),
+        "select_blocks out on host": lambda: saq.select_blocks(q, k, 0.5, 64, out=mask.cpu()),
+        "select_blocks workspace on host": lambda: saq.select_blocks(q, k, 0.5, 64, workspace=ws.cpu()),
+        "select_blocks workspace strided": lambda: saq.select_blocks(q, k, 0.5, 64, workspace=ws[::2]),
+        "select_blocks_pooled workspace on host": lambda: saq.select_blocks_pooled(q.shape, 0.5, ws.cpu(), 64),
+        "select_blocks_pooled out on host":
+            lambda: saq.select_blocks_pooled(q.shape, 0.5, ws, 64, out=torch.empty((B, H, nB, nB), dtype=torch.uint8)),
+        "pooled_change on host": lambda: saq.pooled_change(ws.cpu(), ws, q.shape, 64),
+        "quantize scales on host":
+            lambda: saq.quantize(q, "int8", 64, scales=torch.empty((B, H, nB), dtype=torch.float32)),
+        "dequantize scales on host":
+            lambda: saq.dequantize(torch.zeros((B, S, H, D), dtype=torch.int8, device=DEV),
+                                   torch.ones((B, H, nB), dtype=torch.float32), "int8", 64),
+        "mask_overlap across devices": lambda: saq.mask_overlap(mask, mask.cpu()),
+    }
+    for what, call in cases.items():
+        with pytest.raises(ValueError):
+            call()
+    log(f"  {len(cases)} host or strided buffers refused before launch")
