@@ -20,8 +20,12 @@
  *    Calls are asynchronous on that stream; the library allocates nothing,
  *    keeps no state between calls and is safe to call from several threads.
  *  - Every argument is validated on the host before any launch; a call that
- *    returns non-zero has launched nothing. Device-side faults surface at the
- *    caller's next synchronisation, as for any HIP launch.
+ *    returns non-zero has launched nothing. Validation covers sizes, ranges,
+ *    alignment and overlap, not where a pointer lives: every buffer must be
+ *    device memory of the current device (hipMalloc or torch's allocator), and
+ *    a host pointer is undefined behaviour that typically faults the kernel.
+ *    Device-side faults surface at the caller's next synchronisation, as for
+ *    any HIP launch.
  *  - Return value: SAQ_OK (0) or a negative SAQ_ERR_* code; nothing crosses
  *    the ABI as an exception. saq_status_string() names the code and
  *    saq_last_hip_error() returns the HIP error of the calling thread's last
