@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import math
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -76,3 +77,37 @@ def oracle_mask(qh: np.ndarray, kh: np.ndarray, block: int, keep: float, heads=N
             pk = oracle.pool_blocks(kh[b, :, h:h + 1], block)[0]
             out[(b, h)] = oracle.select_topk(oracle.block_scores(pq, pk), kk)
     return out
+
+
+def oracle_head_masks(qh: torch.Tensor, kh: torch.Tensor, block: int, keeps, heads, b: int = 0, workers: int = 8):
+    """Oracle masks of whole heads of a large layer: {keep: {h: uint8 [nB, nB]}}.
+
+    qh, kh: the GPU's bf16 q-hat / k-hat copied to the host, [B, S, H, D]. Each head is pooled and scored
+    once and selected at every keep ratio; heads run on a thread pool (NumPy releases the GIL in its array
+    loops). The exactness precondition of the pooled sums is asserted on every head."""
+    nB = -(-qh.shape[1] // block)
+
+    def one(h):
+        q64 = qh[b, :, h].double().numpy()[:, None, :]
+        k64 = kh[b, :, h].double().numpy()[:, None, :]
+        assert pooled_exactness_ok(q64) and pooled_exactness_ok(k64), f"head {h}: pooled sums not exact"
+        s = oracle.block_scores(oracle.pool_blocks(q64, block)[0], oracle.pool_blocks(k64, block)[0])
+        return {kp: oracle.select_topk(s, oracle.num_kept_blocks(kp, nB)) for kp in keeps}
+
+    heads = list(heads)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(one, heads))
+    return {kp: {h: r[kp] for h, r in zip(heads, res)} for kp in keeps}
+
+
+def oracle_head_attention(qh: torch.Tensor, kh: torch.Tensor, v: torch.Tensor, mask_h: np.ndarray, block: int,
+                          h: int, b: int = 0) -> np.ndarray:
+    """The oracle's output for every query block of one head, [S, D] fp64 (BLAS does the threading)."""
+    S = qh.shape[1]
+    nB = -(-S // block)
+    q64 = qh[b:b + 1, :, h:h + 1].double().numpy()
+    k64 = kh[b:b + 1, :, h:h + 1].double().numpy()
+    v64 = v[b:b + 1, :, h:h + 1].double().numpy()
+    rows = oracle.block_sparse_attention_rows(q64, k64, v64, mask_h[None, None], block,
+                                              [(0, 0, i) for i in range(nB)])
+    return rows.reshape(nB * block, -1)[:S]

@@ -55,6 +55,7 @@ def test_fused_equals_separate_and_oracle(name):
 @pytest.mark.parametrize("S,H,D,block,keep,grid", [
     (1000, 3, 128, 128, 0.3, (2, 12, 16)),
     (1000, 2, 64, 64, 0.5, (4, 8, 16)),
+    (1000, 2, 64, 128, 0.3, (4, 8, 16)),      # head_dim 64 with block 128 (last block 104 tokens)
     (1, 1, 128, 64, 1.0, (0, 1, 1)),
     (200, 64, 128, 64, 0.2, (2, 5, 10)),      # H*D = 8192, the fused path's limit
 ])

@@ -1,12 +1,16 @@
 """GPU parity at the medium, full (127,040-token) and sweep sizes, in the launch
 configuration the bench times (block 128, head_dim 128).
 
-The oracle cannot redo a whole full-size layer in seconds, so it checks
-samples: prologue rows of selected tokens, masks of selected heads (bit-exact,
-from the GPU's own bf16 q_hat/k_hat), and attention outputs of selected query
-blocks (first, last/partial, the block that mixes video and audio, audio
-blocks, seeded random ones). Properties that hold at any size are checked on
-every output: finite, and inside the per-(head, channel) range of V.
+Masks are compared bit for bit with the oracle's on every head (the oracle
+pools, scores and selects from the GPU's own bf16 q_hat/k_hat, one head per
+thread): at the medium size, at the full size, and at every keep ratio of the
+sweep on one step. Attention is compared with the oracle on whole heads (every
+query block of a head: two heads at the full size, one at each medium keep
+ratio, one at the sweep's keep 0.1) and on sampled query blocks elsewhere
+(first, last/partial, the block that mixes video and audio, audio blocks,
+seeded random ones). Prologue rows are checked on sampled tokens. Properties
+that hold at any size are checked on every output: finite, and inside the
+per-(head, channel) range of V.
 """
 import numpy as np
 import pytest
@@ -15,7 +19,8 @@ import torch
 import oracle
 import sparse_attention_qknorm_amd as saq
 from sparse_attention_qknorm_amd import synth
-from parity_tools import check_attention, check_prologue, log, oracle_mask, pooled_exactness_ok, to64
+from parity_tools import (check_attention, check_prologue, log, oracle_head_attention, oracle_head_masks,
+                          to64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -72,14 +77,23 @@ def _check_masks(layer, mask, keep, heads):
     m_gpu = mask.cpu().numpy()
     kk = saq.kept_blocks(keep, cfg.nB)
     assert (m_gpu.sum(axis=-1) == kk).all() and (np.diagonal(m_gpu, axis1=2, axis2=3) == 1).all()
+    heads = list(heads)
+    ref = oracle_head_masks(qh, kh, cfg.block, [keep], heads)[keep]
     for h in heads:
-        q64 = qh[:, :, h:h + 1].double().numpy()
-        k64 = kh[:, :, h:h + 1].double().numpy()
-        assert pooled_exactness_ok(q64) and pooled_exactness_ok(k64)
-        ref = oracle_mask(q64, k64, cfg.block, keep)[(0, 0)]
-        assert np.array_equal(m_gpu[0, h], ref), f"{cfg.name} keep={keep}: mask differs on head {h}"
-    log(f"  {cfg.name} keep={keep}: masks bit-exact on heads {list(heads)}; k={kk} per row everywhere")
+        assert np.array_equal(m_gpu[0, h], ref[h]), f"{cfg.name} keep={keep}: mask differs on head {h}"
+    log(f"  {cfg.name} keep={keep}: masks bit-exact on {len(heads)} heads {_span(heads)}; k={kk} per row everywhere")
     return m_gpu
+
+
+def _span(heads):
+    return f"{heads[0]}..{heads[-1]}" if len(heads) > 3 else str(heads)
+
+
+def _check_whole_head(layer, m_gpu, o, h, what):
+    """Every query block of head h against the oracle."""
+    qh, kh = layer.host_qk()
+    ref = oracle_head_attention(qh, kh, layer.inp["v"], m_gpu[0, h], layer.cfg.block, h)
+    check_attention(to64(o[0, :, h]), ref, f"{what} head {h} (all {layer.cfg.nB} query blocks)")
 
 
 def _check_attention_sample(layer, m_gpu, o, rows, what):
@@ -149,6 +163,7 @@ def test_medium_select_and_attention(medium, keep):
         m_gpu = _check_masks(medium, mask, keep, range(medium.cfg.H))
     _check_properties(medium, o)
     _check_attention_sample(medium, m_gpu, o, _rows(medium.cfg, 16, 2, [0, 7, 23]), f"medium keep={keep} o")
+    _check_whole_head(medium, m_gpu, o, 7, f"medium keep={keep} o")
 
 
 @pytest.fixture(scope="module")
@@ -162,31 +177,37 @@ def test_full_prologue_sampled(full):
     _check_prologue_sample(full, 3)
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(400)
 def test_full_select_and_attention(full):
     keep = full.cfg.keep_ratios[0]
     mask, o = full.run(keep)
-    m_gpu = _check_masks(full, mask, keep, [0, 13, 39])
+    m_gpu = _check_masks(full, mask, keep, range(full.cfg.H))
     _check_properties(full, o)
-    _check_attention_sample(full, m_gpu, o, _rows(full.cfg, 6, 4, [0, 39]), "full keep=0.15 o")
+    _check_attention_sample(full, m_gpu, o, _rows(full.cfg, 12, 4, [3, 13, 26]), "full keep=0.15 o")
+    for h in (0, 39):
+        _check_whole_head(full, m_gpu, o, h, "full keep=0.15 o")
     # the same launch twice gives the same bytes
     mask2, o2 = full.run(keep)
     assert torch.equal(mask, mask2) and torch.equal(o, o2)
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(500)
 @pytest.mark.parametrize("step", [1, 7])
 def test_sweep_step(step):
+    # every keep ratio of the sweep; on step 7 the masks of all heads and one whole head of attention at
+    # keep 0.1, on step 1 sampled heads
     cfg = synth.get_config("sweep")
     log(f"[sweep] generating step {step}")
     layer = Layer(synth.make_sweep_inputs(cfg, step))
-    for keep in (0.1, 0.3):
+    heads = list(range(cfg.H)) if step == 7 else [5, 20, 33]
+    for keep in cfg.keep_ratios:
         mask, o = layer.run(keep)
-        m_gpu = _check_masks(layer, mask, keep, [5])
-        if keep == 0.3:
-            _check_properties(layer, o)
-            _check_attention_sample(layer, m_gpu, o, [(0, 5, 0), (0, 5, 976), (0, 5, 992), (0, 5, 500)],
-                                    f"sweep step {step} keep={keep} o")
+        m_gpu = _check_masks(layer, mask, keep, heads)
+        _check_properties(layer, o)
+        _check_attention_sample(layer, m_gpu, o, [(0, 5, 0), (0, 5, 976), (0, 5, 992), (0, 5, 500), (0, 31, 77)],
+                                f"sweep step {step} keep={keep} o")
+        if step == 7 and keep == min(cfg.keep_ratios):
+            _check_whole_head(layer, m_gpu, o, 5, f"sweep step {step} keep={keep} o")
 
 
 @pytest.mark.timeout(300)

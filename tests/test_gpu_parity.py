@@ -77,6 +77,8 @@ def test_small_config_end_to_end():
 @pytest.mark.parametrize("S,H,D,block,keep,grid", [
     (1000, 2, 64, 64, 0.5, (4, 8, 16)),      # partial last block (40 tokens), audio tail
     (1000, 3, 128, 128, 0.3, (2, 12, 16)),   # partial last block (104 tokens), odd head count
+    (1000, 2, 64, 128, 0.3, (4, 8, 16)),     # head_dim 64 with block 128
+    (1280, 1, 64, 128, 0.5, (2, 8, 40)),     # head_dim 64 with block 128, whole blocks only
     (127, 1, 64, 64, 1.0, (1, 8, 8)),        # two blocks, keep all
     (1, 1, 128, 128, 0.5, (0, 1, 1)),        # a single token: nB = 1
     (200, 2, 128, 64, 0.01, (2, 5, 10)),     # k = 1: the diagonal only
@@ -104,6 +106,35 @@ def test_constant_inputs_tie_break():
     for i in range(10):
         want = {i} | set([j for j in range(10) if j != i][:3])
         assert set(np.nonzero(mask[0, 0, i])[0].tolist()) == want
+
+
+def test_zero_score_ties():
+    # Scores that tie at exactly zero, next to positive and negative ones. Key blocks 2, 5 and 7 are all
+    # zero (stored as -0.0 in head 0 and +0.0 in head 1), so every row scores them +0.0; query block 3 is
+    # zero too (signed zeros again), so its row ties everywhere and keeps the lowest indices; key blocks 4
+    # and 8 repeat block 1 exactly (equal non-zero scores); the rest are random, so some rows rank the zero
+    # blocks above negative scores and below positive ones. The mask must be the oracle's, bit for bit.
+    S, H, D, block, nB = 640, 2, 64, 64, 10
+    rng = np.random.Generator(np.random.PCG64(21))
+    q = torch.from_numpy(rng.standard_normal((1, S, H, D)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((1, S, H, D)).astype(np.float32)).to(torch.bfloat16)
+    for h, z in ((0, -0.0), (1, 0.0)):
+        for j in (2, 5, 7):
+            k[0, j * block:(j + 1) * block, h] = z
+        q[0, 3 * block:4 * block, h] = z
+        q[0, 3 * block:4 * block:2, h, ::3] = -z
+    for j in (4, 8):
+        k[0, j * block:(j + 1) * block] = k[0, block:2 * block]
+    assert (k[0, 2 * block:3 * block, 0].view(torch.int16) == -32768).all()     # really -0.0
+    for keep in (0.3, 0.5, 0.8):
+        mask = saq.select_blocks(q.to(DEV), k.to(DEV), keep, block).cpu().numpy()
+        ref = oracle_mask(to64(q), to64(k), block, keep)
+        for (b, h), m in ref.items():
+            assert np.array_equal(mask[b, h], m), f"keep={keep}: mask differs on head {h}"
+        kk = saq.kept_blocks(keep, nB)
+        for h in range(H):
+            assert set(np.nonzero(mask[0, h, 3])[0].tolist()) == {3} | set([j for j in range(nB) if j != 3][:kk - 1])
+    log("  zero-score ties (signed-zero inputs), repeated blocks: masks equal the oracle's at keep 0.3/0.5/0.8")
 
 
 def test_user_mask_with_empty_rows_and_all_ones():
