@@ -190,7 +190,10 @@ def sweep(args) -> dict:
         pending = []
         for kp in keeps:
             ev_fresh = timed(lambda: saq.select_blocks_pooled(shape, kp, cur, cfg.block, out=fresh[kp]))
-            ent = {"fresh_select": ev_fresh, "thr": {}}
+            # attention on the fresh mask: the per-step select + attention time with the selection redone
+            # every step
+            ev_fresh_att = timed(lambda: saq.block_sparse_attn(qh, kh, x["v"], fresh[kp], cfg.block, out=o_fresh))
+            ent = {"fresh_select": ev_fresh, "fresh_attn": ev_fresh_att, "thr": {}}
             if step:
                 ent["overlap_prev"] = saq.mask_overlap(fresh[kp], prev_fresh[kp])
             for t in thresholds:
@@ -200,7 +203,6 @@ def sweep(args) -> dict:
                 te = {"sel": ev_sel, "att": ev_att, "ov_fresh": saq.mask_overlap(r.mask, fresh[kp])}
                 torch.cuda.synchronize()
                 if not r.recomputed():
-                    saq.block_sparse_attn(qh, kh, x["v"], fresh[kp], cfg.block, out=o_fresh)
                     diff = (o_used.float() - o_fresh.float())
                     te["err"] = (float(diff.abs().max().item()),
                                  float(diff.norm().item() / max(o_fresh.float().norm().item(), 1e-30)))
@@ -220,6 +222,8 @@ def sweep(args) -> dict:
         for kp, ent in row["per_keep"].items():
             ent["fresh_ms"] = ent.pop("fresh_select")
             ent["fresh_ms"] = ent["fresh_ms"][0].elapsed_time(ent["fresh_ms"][1])
+            ent["fresh_attn_ms"] = ent.pop("fresh_attn")
+            ent["fresh_attn_ms"] = ent["fresh_attn_ms"][0].elapsed_time(ent["fresh_attn_ms"][1])
             if "overlap_prev" in ent:
                 c = ent["overlap_prev"].sum(dim=(0, 1)).tolist()
                 ent["overlap_prev"] = c[0] / c[1]
@@ -230,7 +234,8 @@ def sweep(args) -> dict:
                 te["att_ms"] = te["att_ms"][0].elapsed_time(te["att_ms"][1])
                 c = te.pop("ov_fresh").sum(dim=(0, 1)).tolist()
                 te["overlap_with_fresh"] = c[0] / c[1]
-            line.append(f"keep {kp}: overlap vs prev {ent.get('overlap_prev', 1.0):.4f}, decisions " +
+            line.append(f"keep {kp}: select {ent['fresh_ms']:.3f} + attention {ent['fresh_attn_ms']:.2f} ms, "
+                        f"overlap vs prev {ent.get('overlap_prev', 1.0):.4f}, decisions " +
                         " ".join(f"{t}:{'R' if te['recomputed'] else 'K'}" for t, te in ent["thr"].items()))
         log("[sweep] " + "; ".join(line))
         rows.append(row)
@@ -254,7 +259,10 @@ def sweep(args) -> dict:
             }
     per_step = [{"step": r["step"], "prologue_pool_ms": r["pro_ms"], "pooled_change_vs_prev": r.get("change_prev"),
                  "mask_overlap_vs_prev": {str(kp): r["per_keep"][kp].get("overlap_prev") for kp in keeps},
-                 "fresh_select_ms": {str(kp): r["per_keep"][kp]["fresh_ms"] for kp in keeps}} for r in rows]
+                 "fresh_select_ms": {str(kp): r["per_keep"][kp]["fresh_ms"] for kp in keeps},
+                 "fresh_attn_ms": {str(kp): r["per_keep"][kp]["fresh_attn_ms"] for kp in keeps},
+                 "fresh_select_plus_attn_ms": {str(kp): r["per_keep"][kp]["fresh_ms"] + r["per_keep"][kp]["fresh_attn_ms"]
+                                               for kp in keeps}} for r in rows]
     return {"workload": f"sweep: {cfg.steps} denoising steps of the full layer (S={cfg.S}, H={cfg.H}, D={cfg.D}), "
                         f"step s = bf16(X_base + {cfg.drift}*s*Delta)",
             "keeps": keeps, "thresholds": thresholds, "per_step": per_step, "summary": summary}
@@ -373,6 +381,8 @@ def main(argv=None) -> int:
                     help="also run a plain 1 GiB read + 1 GiB write elementwise copy (3 launches) after the timed "
                          "steps, as the reference kernel for scaling HBM byte counters")
     args = ap.parse_args(argv)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the layer would shard by "
@@ -432,9 +442,8 @@ def main(argv=None) -> int:
         if record:
             e[2].record(stream)
         if args.path == "folded":
-            # the selection runs inside the attention kernel; the mask is written only on the first
-            # (untimed) call, for the FLOP count
-            saq.block_sparse_attn_select(qh, kh, v, ws, keep, cfg.block, out=o, mask_out=None if record else mask)
+            # the selection runs inside the attention kernel; no mask is written in the timed steps
+            saq.block_sparse_attn_select(qh, kh, v, ws, keep, cfg.block, out=o, mask_out=None)
         else:
             saq.block_sparse_attn(qh, kh, v, mask, cfg.block, out=o)
         if record:
@@ -447,8 +456,6 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    flops = computed_flops(mask, cfg.S, cfg.block, cfg.D)
-    dense_flops = 4.0 * cfg.D * cfg.H * cfg.B * float(cfg.S) ** 2
 
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -458,6 +465,13 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    # FLOPs from the mask the timed steps used: the fused and split paths write it every step; the folded
+    # path writes it only when asked, so one more (untimed) call fills it
+    if args.path == "folded":
+        saq.block_sparse_attn_select(qh, kh, v, ws, keep, cfg.block, out=o, mask_out=mask)
+        torch.cuda.synchronize()
+    flops = computed_flops(mask, cfg.S, cfg.block, cfg.D)
+    dense_flops = 4.0 * cfg.D * cfg.H * cfg.B * float(cfg.S) ** 2
 
     def avg_ms(name):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
