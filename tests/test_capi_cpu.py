@@ -59,10 +59,17 @@ def test_kept_blocks_errors():
 
 def test_workspace_bytes():
     lib = _binding.lib()
+    # pooled means of q and k (padded to 256 bytes), then for nB <= 1024 the k means transposed with nB
+    # padded to 256/512/1024, beyond that the uint64 score keys
     nB = 993
-    pooled = 2 * 40 * nB * 128 * 8
-    want = (pooled + 255) // 256 * 256 + 40 * nB * nB * 8
-    assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 128, 128) == want
+    pooled = (2 * 40 * nB * 128 * 8 + 255) // 256 * 256
+    assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 128, 128) == pooled + 40 * 128 * 1024 * 8
+    nB = 200
+    pooled = (2 * 3 * nB * 64 * 8 + 255) // 256 * 256
+    assert lib.saq_select_blocks_workspace_bytes(1, 200 * 64, 3, 64, 64) == pooled + 3 * 64 * 256 * 8
+    nB = 2000
+    pooled = (2 * 2 * nB * 128 * 8 + 255) // 256 * 256
+    assert lib.saq_select_blocks_workspace_bytes(1, 2000 * 128, 2, 128, 128) == pooled + 2 * nB * nB * 8
     assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 96, 128) == 0     # unsupported D
     assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 128, 32) == 0     # unsupported block
     assert lib.saq_select_blocks_workspace_bytes(1, 0, 40, 128, 128) == 0
