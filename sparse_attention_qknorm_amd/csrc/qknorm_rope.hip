@@ -24,6 +24,43 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBatch = 4;   // 16-byte chunks kept in flight per thread
 
+// QKNorm + RoPE of one 16-byte chunk (8 channels) of a (token, head) row, the
+// row spread over `lanes_per_row` adjacent lanes. Both prologue kernels call
+// this one routine, with contraction into FMA switched off, so they produce
+// the same bits. With kAcc, the rounded bf16 outputs are also added to acc in
+// fp64 (exact for these values).
+template <bool kAcc>
+__device__ __forceinline__ uint4 norm_rope_chunk(const uint4 raw, const float (&w)[8], const float2 (&rot)[4],
+                                                 float eps, float inv_d, int lanes_per_row, double (&acc)[8]) {
+#pragma clang fp contract(off)
+    const uint32_t w32[4] = {raw.x, raw.y, raw.z, raw.w};
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_bits_to_f32(w32[e] & 0xffffu);
+        x[2 * e + 1] = bf16_bits_to_f32(w32[e] >> 16);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = ss + x[e] * x[e];
+    for (int off = lanes_per_row / 2; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off, lanes_per_row);
+    const float rinv = 1.0f / sqrtf(ss * inv_d + eps);
+    uint32_t outw[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float y0 = x[2 * p] * rinv * w[2 * p];
+        const float y1 = x[2 * p + 1] * rinv * w[2 * p + 1];
+        const uint32_t h0 = f32_to_bf16_bits(y0 * rot[p].x - y1 * rot[p].y);
+        const uint32_t h1 = f32_to_bf16_bits(y0 * rot[p].y + y1 * rot[p].x);
+        outw[p] = h0 | (h1 << 16);
+        if constexpr (kAcc) {
+            acc[2 * p] += (double)bf16_bits_to_f32(h0);
+            acc[2 * p + 1] += (double)bf16_bits_to_f32(h1);
+        }
+    }
+    return make_uint4(outw[0], outw[1], outw[2], outw[3]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(
     const uint4* q_in, const uint4* k_in, uint4* q_out, uint4* k_out,
@@ -77,29 +114,11 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(
             // Whole rows are in or out together (total and the stride are multiples of a row).
             if (c < total) {
                 const bool is_q = c < chunks_per_tensor;
-                const uint32_t w32[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-                float x[8];
+                float w[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[2 * e] = bf16_bits_to_f32(w32[e] & 0xffffu);
-                    x[2 * e + 1] = bf16_bits_to_f32(w32[e] >> 16);
-                }
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-#pragma unroll
-                for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kLanesPerRow);
-                const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-                uint32_t outw[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float y0 = x[2 * p] * rinv * (is_q ? wq[2 * p] : wk[2 * p]);
-                    const float y1 = x[2 * p + 1] * rinv * (is_q ? wq[2 * p + 1] : wk[2 * p + 1]);
-                    const float r0 = y0 * rot[p].x - y1 * rot[p].y;
-                    const float r1 = y0 * rot[p].y + y1 * rot[p].x;
-                    outw[p] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-                }
-                const uint4 o = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+                for (int e = 0; e < 8; ++e) w[e] = is_q ? wq[e] : wk[e];
+                double unused[8];
+                const uint4 o = norm_rope_chunk<false>(raw[j], w, rot, eps, 1.0f / D, kLanesPerRow, unused);
                 if (is_q) q_out[base + c] = o;
                 else k_out[base + c - chunks_per_tensor] = o;
             }
@@ -136,27 +155,30 @@ namespace {
 // covering every head: one thread per 16-byte chunk position (head, 8
 // channels) of a token row, H*D/8 of them (rounded up to whole wavefronts),
 // each handling that position of both q and k for the whole block. The
-// workgroup walks the block's tokens one at a time, applies QKNorm + RoPE
-// exactly as the per-token kernel above (same arithmetic, same bits), writes
-// the bf16 results, and accumulates the rounded bf16 values it wrote in fp64.
-// Sums of bf16 values with |x| < 16 are exact in fp64, so the means equal those
-// of the separate pooling pass bit for bit, and the pass saves that pass's
-// re-read of q-hat and k-hat. Each token's rotation angles are computed once
-// (fp64 sincos, staged in LDS kTokChunk tokens at a time) for all heads of q
-// and k. Measured at the full shape: one token per step and whole rows per
-// workgroup beat splitting the heads over workgroups or keeping more tokens in
-// flight per thread.
+// workgroup walks the block's tokens, applies QKNorm + RoPE exactly as the
+// per-token kernel above (same arithmetic, same bits), writes the bf16
+// results, and accumulates the rounded bf16 values it wrote in fp64. Sums of
+// bf16 values with |x| < 16 are exact in fp64, so the means equal those of the
+// separate pooling pass bit for bit, and the pass saves that pass's re-read of
+// q-hat and k-hat. The walk is software-pipelined: the loads of the next
+// kDepth tokens are in flight while a token is processed, across the chunk
+// boundaries too, and the rotation angles (fp64 sincos, computed once per token
+// for all heads of q and k) are staged in two LDS buffers of kTokChunk tokens,
+// the next chunk's computed while the current one is used.
 constexpr int kPoolMaxThreads = 1024;                          // H*D <= 8192
 
-template <int D>
-__global__ __launch_bounds__(kPoolMaxThreads) void qknorm_rope_pool_kernel(
+
+// kDepth: tokens in flight ahead of the one processed; kMaxThreads bounds the
+// workgroup (and so the registers available per thread).
+template <int D, int kMaxThreads, int kDepth>
+__global__ __launch_bounds__(kMaxThreads) void qknorm_rope_pool_kernel(
     const uint4* q_in, const uint4* k_in, uint4* q_out, uint4* k_out, const int32_t* __restrict__ pos_thw,
     const float* __restrict__ w_q, const float* __restrict__ w_k, int32_t S, int32_t H, RopeTable table, float eps,
     int32_t block, int32_t nB, double* __restrict__ pooled) {
     constexpr int kLanesPerRow = D / 8;
     constexpr int kPairs = D / 2;
-    constexpr int kTokChunk = 32;                              // tokens whose angles are staged at once
-    __shared__ float2 cs[kTokChunk][kPairs];
+    constexpr int kTokChunk = 16;                              // tokens whose angles are staged at once
+    __shared__ float2 cs[2][kTokChunk][kPairs];
 
     const int T = (int)blockDim.x;
     const int64_t bi = blockIdx.x;                             // b * nB + i
@@ -164,81 +186,87 @@ __global__ __launch_bounds__(kPoolMaxThreads) void qknorm_rope_pool_kernel(
     const int64_t b = bi / nB;
     const int t0 = i * block;
     const int t1 = min(t0 + block, S);
+    const int n = t1 - t0;
     const int tid = threadIdx.x;
     const int P = H * kLanesPerRow;                            // chunk positions per token row
     const bool active = tid < P;                               // whole rows in or out together
     const int lane_in_row = tid % kLanesPerRow;
-    float wq[8], wk[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        wq[e] = w_q[lane_in_row * 8 + e];
-        wk[e] = w_k[lane_in_row * 8 + e];
-    }
-    double acc[2][8];                                          // [tensor][channel]
-#pragma unroll
-    for (int ten = 0; ten < 2; ++ten)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[ten][e] = 0.0;
 
-    for (int tc = t0; tc < t1; tc += kTokChunk) {
+    auto stage_angles = [&](int c) {                           // chunk c of the block into buffer c % 2
+        const int tc = t0 + c * kTokChunk;
         const int nt = min(kTokChunk, t1 - tc);
-        __syncthreads();                                       // previous chunk's angles consumed
         for (int wi = tid; wi < nt * kPairs; wi += T) {
             const int tt = wi / kPairs, p = wi % kPairs;
             const int axis = p < table.pair_end_t ? 0 : (p < table.pair_end_h ? 1 : 2);
             const double theta = (double)pos_thw[(int64_t)(tc + tt) * 3 + axis] * table.inv_freq[p];
             double sn, cn;
             sincos(theta, &sn, &cn);
-            cs[tt][p] = make_float2((float)cn, (float)sn);
+            cs[c & 1][tt][p] = make_float2((float)cn, (float)sn);
         }
-        __syncthreads();
-        if (!active) continue;
-        for (int ts = 0; ts < nt; ++ts) {
-            const int64_t at = (b * S + tc + ts) * (int64_t)P + tid;
-            const uint4 raw[2] = {q_in[at], k_in[at]};
+    };
+
+    float wq[8], wk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        wq[e] = w_q[lane_in_row * 8 + e];
+        wk[e] = w_k[lane_in_row * 8 + e];
+    }
+    double accq[8], acck[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accq[e] = acck[e] = 0.0;
+
+    const int64_t row0 = (b * S + t0) * (int64_t)P + tid;       // position tid of token t0
+    uint4 rq[kDepth], rk[kDepth];                               // the next kDepth tokens, oldest first
+    if (active) {
+#pragma unroll
+        for (int a = 0; a < kDepth; ++a)
+            if (a < n) {
+                rq[a] = q_in[row0 + (int64_t)a * P];
+                rk[a] = k_in[row0 + (int64_t)a * P];
+            }
+    }
+    const uint4* qsrc = q_in + row0 + (int64_t)kDepth * P;     // token t + kDepth
+    const uint4* ksrc = k_in + row0 + (int64_t)kDepth * P;
+    uint4* qdst = q_out + row0;                                // token t
+    uint4* kdst = k_out + row0;
+    stage_angles(0);
+    for (int t = 0; t < n; ++t) {
+        const int tt = t % kTokChunk;
+        if (tt == 0) {
+            __syncthreads();                                   // this chunk staged; the other buffer free
+            if (t + kTokChunk < n) stage_angles(t / kTokChunk + 1);
+        }
+        if (active) {
+            const uint4 cq = rq[0], ck = rk[0];
+#pragma unroll
+            for (int a = 0; a + 1 < kDepth; ++a) {
+                rq[a] = rq[a + 1];
+                rk[a] = rk[a + 1];
+            }
+            if (t + kDepth < n) {
+                rq[kDepth - 1] = *qsrc;
+                rk[kDepth - 1] = *ksrc;
+            }
+            qsrc += P;
+            ksrc += P;
             float2 rot[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) rot[p] = cs[ts][lane_in_row * 4 + p];
-#pragma unroll
-            for (int ten = 0; ten < 2; ++ten) {
-                const uint32_t w32[4] = {raw[ten].x, raw[ten].y, raw[ten].z, raw[ten].w};
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[2 * e] = bf16_bits_to_f32(w32[e] & 0xffffu);
-                    x[2 * e + 1] = bf16_bits_to_f32(w32[e] >> 16);
-                }
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-#pragma unroll
-                for (int off = kLanesPerRow / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kLanesPerRow);
-                const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-                uint32_t outw[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float y0 = x[2 * p] * rinv * (ten == 0 ? wq[2 * p] : wk[2 * p]);
-                    const float y1 = x[2 * p + 1] * rinv * (ten == 0 ? wq[2 * p + 1] : wk[2 * p + 1]);
-                    const uint32_t h0 = f32_to_bf16_bits(y0 * rot[p].x - y1 * rot[p].y);
-                    const uint32_t h1 = f32_to_bf16_bits(y0 * rot[p].y + y1 * rot[p].x);
-                    outw[p] = h0 | (h1 << 16);
-                    acc[ten][2 * p] += (double)bf16_bits_to_f32(h0);
-                    acc[ten][2 * p + 1] += (double)bf16_bits_to_f32(h1);
-                }
-                const uint4 o = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-                if (ten == 0) q_out[at] = o;
-                else k_out[at] = o;
-            }
+            for (int p = 0; p < 4; ++p) rot[p] = cs[(t / kTokChunk) & 1][tt][lane_in_row * 4 + p];
+            *qdst = norm_rope_chunk<true>(cq, wq, rot, eps, 1.0f / D, kLanesPerRow, accq);
+            *kdst = norm_rope_chunk<true>(ck, wk, rot, eps, 1.0f / D, kLanesPerRow, acck);
+            qdst += P;
+            kdst += P;
         }
     }
     if (!active) return;
     const int64_t Bsz = gridDim.x / nB;
     const int h = tid / kLanesPerRow;
+    double* outq = pooled + (((int64_t)0 * Bsz + b) * H + h) * nB * (int64_t)D + (int64_t)i * D + lane_in_row * 8;
+    double* outk = pooled + (((int64_t)1 * Bsz + b) * H + h) * nB * (int64_t)D + (int64_t)i * D + lane_in_row * 8;
 #pragma unroll
-    for (int ten = 0; ten < 2; ++ten) {
-        double* out = pooled + ((((int64_t)ten * Bsz + b) * H + h) * nB + i) * (int64_t)D + lane_in_row * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = acc[ten][e] / (double)(t1 - t0);
+    for (int e = 0; e < 8; ++e) {
+        outq[e] = accq[e] / (double)n;
+        outk[e] = acck[e] / (double)n;
     }
 }
 
@@ -248,9 +276,15 @@ void launch_pool_d(const void* q_in, const void* k_in, void* q_out, void* k_out,
                    float eps, int32_t block, int32_t nB, double* pooled, hipStream_t stream) {
     const int P = H * (D / 8);                                 // <= kMaxRowElems / 8 = 1024
     const int T = ((P + kWave - 1) / kWave) * kWave;
-    hipLaunchKernelGGL((qknorm_rope_pool_kernel<D>), dim3((unsigned)((int64_t)B * nB)), dim3(T), 0, stream,
-                       (const uint4*)q_in, (const uint4*)k_in, (uint4*)q_out, (uint4*)k_out, pos_thw, w_q, w_k, S,
-                       H, table, eps, block, nB, pooled);
+    const dim3 grid((unsigned)((int64_t)B * nB));
+    if (T <= 768)       // up to 12 wavefronts: room for three tokens in flight
+        hipLaunchKernelGGL((qknorm_rope_pool_kernel<D, 768, 3>), grid, dim3(T), 0, stream, (const uint4*)q_in,
+                           (const uint4*)k_in, (uint4*)q_out, (uint4*)k_out, pos_thw, w_q, w_k, S, H, table, eps,
+                           block, nB, pooled);
+    else
+        hipLaunchKernelGGL((qknorm_rope_pool_kernel<D, kPoolMaxThreads, 1>), grid, dim3(T), 0, stream,
+                           (const uint4*)q_in, (const uint4*)k_in, (uint4*)q_out, (uint4*)k_out, pos_thw, w_q, w_k,
+                           S, H, table, eps, block, nB, pooled);
 }
 
 }  // namespace
