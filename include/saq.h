@@ -136,6 +136,25 @@ int saq_select_blocks(const void* q, const void* k, int32_t B, int32_t S, int32_
                       size_t workspace_bytes, void* stream);
 
 /*
+ * saq_select_blocks for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same selection, the same mask bit for bit, with the workspace taken from
+ * a scratch array the library holds in device memory, one copy per GPU, from
+ * the library's load until the process ends. Sizes whose workspace
+ * (saq_select_blocks_workspace_bytes) exceeds SAQ_NOALLOC_SCRATCH_BYTES are
+ * rejected with SAQ_ERR_WORKSPACE before any HIP call; the full 127,040-token,
+ * 40-head layer at block 128 needs 123 MB and fits. The call allocates
+ * nothing. Every call on one GPU uses that GPU's one array, so calls that
+ * overlap in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller; successive calls on one stream are safe. Arguments
+ * and other errors as saq_select_blocks; the first call on a device may also
+ * return SAQ_ERR_HIP if the array's address cannot be obtained.
+ */
+#define SAQ_NOALLOC_SCRATCH_BYTES (128u << 20)
+int saq_select_blocks_noalloc(const void* q, const void* k, int32_t B, int32_t S, int32_t H, int32_t D,
+                              int32_t block, double keep_ratio, uint8_t* block_mask, void* stream);
+
+/*
  * Block-sparse flash attention (Sol-Attn paragraph of the Sol Engine "H3 on
  * device" page: attention computed only on the kept blocks, with an online
  * softmax). For each (b, h, query block i), over the kept key blocks j in

@@ -29,6 +29,7 @@ import torch
 from ._binding import SaqError, check, lib
 
 __all__ = ["qknorm_rope", "qknorm_rope_out", "qknorm_rope_pool", "select_blocks", "select_blocks_pooled",
+           "select_blocks_noalloc",
            "select_workspace_bytes", "block_sparse_attn", "kept_blocks", "mask_overlap", "pooled_change", "pooled_bytes",
            "MaskReuse", "quantize", "dequantize", "block_sparse_attn_select", "attention_layer",
            "SaqError", "lib"]
@@ -169,6 +170,25 @@ def select_blocks(q: torch.Tensor, k: torch.Tensor, keep_ratio: float, block: in
     st = lib().saq_select_blocks(q.data_ptr(), k.data_ptr(), B, S, H, D, block, float(keep_ratio), out.data_ptr(),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
     check(st, "saq_select_blocks")
+    return out
+
+
+def select_blocks_noalloc(q: torch.Tensor, k: torch.Tensor, keep_ratio: float, block: int = 128,
+                          out: torch.Tensor = None) -> torch.Tensor:
+    """select_blocks with the library's own device scratch instead of a workspace (saq_select_blocks_noalloc).
+    With `out` given, nothing is allocated. Calls that overlap on one GPU race (one scratch per GPU)."""
+    _check_qkv("q", q)
+    _check_qkv("k", k, q)
+    B, S, H, D = q.shape
+    nB = -(-S // block)
+    if out is None:
+        out = torch.empty((B, H, nB, nB), dtype=torch.uint8, device=q.device)
+    elif out.dtype != torch.uint8 or tuple(out.shape) != (B, H, nB, nB) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 [B,H,nB,nB] tensor")
+    _check_buf("out", out, q.device)
+    st = lib().saq_select_blocks_noalloc(q.data_ptr(), k.data_ptr(), B, S, H, D, block, float(keep_ratio),
+                                         out.data_ptr(), _stream(q))
+    check(st, "saq_select_blocks_noalloc")
     return out
 
 

@@ -33,6 +33,7 @@ SIGNATURES = [
     ("saq_kept_blocks", _i32, [_f64, _i32]),
     ("saq_select_blocks_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]),
     ("saq_select_blocks", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp, _sz, _vp]),
+    ("saq_select_blocks_noalloc", ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp]),
     ("saq_block_sparse_attn", ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp]),
     ("saq_qknorm_rope_pool", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f64, _f64, _i32, _vp, _sz, _vp]),

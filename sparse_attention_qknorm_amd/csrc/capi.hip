@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/saq.h"
 #include "kernels.h"
 
@@ -322,6 +324,73 @@ int saq_select_blocks(const void* q, const void* k, int32_t B, int32_t S, int32_
     if (st) return st;
     return finish(saq::launch_select_blocks(q, k, B, S, H, D, block, kept, block_mask, workspace,
                                             (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Block selection without a caller workspace (saq_select_blocks_noalloc): its
+// scratch is this file-scope device array. Each GPU the library runs on holds
+// its own copy from the module's load until the process ends; the host learns
+// that copy's address once per device with hipGetSymbolAddress (the array's
+// name is not a device address in host code) and passes only that address to
+// the kernels.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[SAQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on the first call on that device.
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return SAQ_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SAQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || p == nullptr) {
+            g_last_hip_error = (int)err;
+            return SAQ_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SAQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int saq_select_blocks_noalloc(const void* q, const void* k, int32_t B, int32_t S, int32_t H, int32_t D,
+                              int32_t block, double keep_ratio, uint8_t* block_mask, void* stream) {
+    if (!q || !k || !block_mask) return SAQ_ERR_NULL;
+    int st = check_dims(B, S, H, D);
+    if (st) return st;
+    st = check_block(S, block);
+    if (st) return st;
+    const int32_t nB = (S + block - 1) / block;
+    const int32_t kept = saq_kept_blocks(keep_ratio, nB);
+    if (kept < 0) return kept;
+    if (!aligned16(q) || !aligned16(k)) return SAQ_ERR_ALIGN;
+    if (saq::select_workspace_bytes(B, H, nB, D) > (size_t)SAQ_NOALLOC_SCRATCH_BYTES) return SAQ_ERR_WORKSPACE;
+    const size_t bytes = (size_t)B * S * H * D * 2;
+    const size_t mbytes = (size_t)B * H * nB * nB;
+    if (overlaps(block_mask, mbytes, q, bytes) || overlaps(block_mask, mbytes, k, bytes)) return SAQ_ERR_ALIAS;
+    st = device_ready();
+    if (st) return st;
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st) return st;
+    return finish(saq::launch_select_blocks(q, k, B, S, H, D, block, kept, block_mask, ws, (hipStream_t)stream));
 }
 
 int saq_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* block_mask, int32_t B,
