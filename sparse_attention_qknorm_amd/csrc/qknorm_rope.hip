@@ -24,34 +24,51 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBatch = 4;   // 16-byte chunks kept in flight per thread
 
+// Sum over the kLanesPerRow (8 or 16) adjacent lanes holding one row, with DPP
+// lane exchanges (no LDS): swap neighbours, swap pairs, mirror the halves of
+// each 8-lane group, then (16 lanes) mirror the two 8-lane groups. Each step
+// adds two equal-shaped partial sums, so every lane ends with the same bits.
+template <int kLanesPerRow>
+__device__ __forceinline__ float row_sum(float v) {
+    static_assert(kLanesPerRow == 8 || kLanesPerRow == 16, "row of 8 or 16 lanes");
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    if constexpr (kLanesPerRow == 16)
+        v = v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // QKNorm + RoPE of one 16-byte chunk (8 channels) of a (token, head) row, the
-// row spread over `lanes_per_row` adjacent lanes. Both prologue kernels call
-// this one routine, with contraction into FMA switched off, so they produce
-// the same bits. With kAcc, the rounded bf16 outputs are also added to acc in
-// fp64 (exact for these values).
-template <bool kAcc>
+// row spread over kLanesPerRow adjacent lanes. Both prologue kernels call this
+// one routine, with contraction into FMA switched off and every FMA written
+// out, so they produce the same bits. The reciprocal square root is the
+// hardware's (within 1 fp32 ulp; the result is rounded to bf16). With kAcc,
+// the rounded bf16 outputs are also added to acc in fp64 (exact for these
+// values).
+template <bool kAcc, int kLanesPerRow>
 __device__ __forceinline__ uint4 norm_rope_chunk(const uint4 raw, const float (&w)[8], const float2 (&rot)[4],
-                                                 float eps, float inv_d, int lanes_per_row, double (&acc)[8]) {
+                                                 float eps, float inv_d, double (&acc)[8]) {
 #pragma clang fp contract(off)
     const uint32_t w32[4] = {raw.x, raw.y, raw.z, raw.w};
     float x[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         x[2 * e] = bf16_bits_to_f32(w32[e] & 0xffffu);
-        x[2 * e + 1] = bf16_bits_to_f32(w32[e] >> 16);
+        x[2 * e + 1] = __uint_as_float(w32[e] & 0xffff0000u);
     }
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = ss + x[e] * x[e];
-    for (int off = lanes_per_row / 2; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off, lanes_per_row);
-    const float rinv = 1.0f / sqrtf(ss * inv_d + eps);
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    ss = row_sum<kLanesPerRow>(ss);
+    const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, inv_d, eps));
     uint32_t outw[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const float y0 = x[2 * p] * rinv * w[2 * p];
         const float y1 = x[2 * p + 1] * rinv * w[2 * p + 1];
-        const uint32_t h0 = f32_to_bf16_bits(y0 * rot[p].x - y1 * rot[p].y);
-        const uint32_t h1 = f32_to_bf16_bits(y0 * rot[p].y + y1 * rot[p].x);
+        const uint32_t h0 = f32_to_bf16_bits(__builtin_fmaf(y0, rot[p].x, -(y1 * rot[p].y)));
+        const uint32_t h1 = f32_to_bf16_bits(__builtin_fmaf(y0, rot[p].y, y1 * rot[p].x));
         outw[p] = h0 | (h1 << 16);
         if constexpr (kAcc) {
             acc[2 * p] += (double)bf16_bits_to_f32(h0);
@@ -118,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) w[e] = is_q ? wq[e] : wk[e];
                 double unused[8];
-                const uint4 o = norm_rope_chunk<false>(raw[j], w, rot, eps, 1.0f / D, kLanesPerRow, unused);
+                const uint4 o = norm_rope_chunk<false, kLanesPerRow>(raw[j], w, rot, eps, 1.0f / D, unused);
                 if (is_q) q_out[base + c] = o;
                 else k_out[base + c - chunks_per_tensor] = o;
             }
@@ -252,8 +269,8 @@ __global__ __launch_bounds__(kMaxThreads) void qknorm_rope_pool_kernel(
             float2 rot[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) rot[p] = cs[(t / kTokChunk) & 1][tt][lane_in_row * 4 + p];
-            *qdst = norm_rope_chunk<true>(cq, wq, rot, eps, 1.0f / D, kLanesPerRow, accq);
-            *kdst = norm_rope_chunk<true>(ck, wk, rot, eps, 1.0f / D, kLanesPerRow, acck);
+            *qdst = norm_rope_chunk<true, kLanesPerRow>(cq, wq, rot, eps, 1.0f / D, accq);
+            *kdst = norm_rope_chunk<true, kLanesPerRow>(ck, wk, rot, eps, 1.0f / D, acck);
             qdst += P;
             kdst += P;
         }
