@@ -268,6 +268,10 @@ __global__ __launch_bounds__(BLOCK * 2) void block_sparse_attn_kernel(
 // used in the exponent only moves (and O is only rescaled) when a tile's max
 // exceeds it by more than 8, so p <= 2^8 and the rescale is almost never paid.
 // Row sums use v_dot2 on the bf16 P, the same values the PV product consumes.
+// Operand reads from LDS run one MFMA step ahead of the MFMAs that use them (the
+// next d-step's K fragments, the next key step's V^T fragments), with the order
+// pinned by scheduling-group barriers; the transposed-V read addresses are
+// precomputed per lane (eight base offsets, the key step only adds 16 rows).
 namespace d128 {
 
 constexpr int kBlock = 128;
@@ -335,6 +339,17 @@ __device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* 
 
     const int krow = swap_bits23(l32);                 // K row this lane feeds as A-operand row l32
     const int kfr = swz(krow);
+    // byte offsets of this lane's transposed V reads: row 16s + 8g + 4hh + jl/4 and chunk 4t + .. of a tile;
+    // the swizzle of those rows does not depend on s, so s only adds 16 rows (4096 bytes)
+    uint32_t voff[2][kD / 32];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int t = 0; t < kD / 32; ++t) {
+            const int r = 8 * g + 4 * hh + jl / 4;
+            const int c = 4 * t + 2 * (grp % 2) + (jl % 4) / 2;
+            voff[hh][t] = (uint32_t)(r * kRowBytes + ((c ^ swz(r)) * 16) + 8 * (jl % 2));
+        }
     float m_used = -INFINITY;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -352,14 +367,29 @@ __device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* 
 #pragma unroll
         for (int kt = 0; kt < kBlock / 32; ++kt) sacc[kt] = (f32x16){};
         const uint8_t* krow_p = k_lds + krow * kRowBytes;
+        // the next d-step's four K fragments are read while this step's four MFMAs run
+        bf16x8 ka[2][kBlock / 32];
+#pragma unroll
+        for (int kt = 0; kt < kBlock / 32; ++kt)
+            ka[0][kt] = *(const bf16x8*)(krow_p + kt * 32 * kRowBytes + ((0 + g) ^ kfr) * 16);
 #pragma unroll
         for (int st = 0; st < kD / 16; ++st) {
-            const int c = (2 * st + g) ^ kfr;
+            if (st + 1 < kD / 16) {
+                const int c = (2 * (st + 1) + g) ^ kfr;
 #pragma unroll
-            for (int kt = 0; kt < kBlock / 32; ++kt) {      // four independent accumulators in turn
-                const bf16x8 a = *(const bf16x8*)(krow_p + kt * 32 * kRowBytes + c * 16);
-                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[st], sacc[kt], 0, 0, 0);
+                for (int kt = 0; kt < kBlock / 32; ++kt)
+                    ka[(st + 1) & 1][kt] = *(const bf16x8*)(krow_p + kt * 32 * kRowBytes + c * 16);
             }
+#pragma unroll
+            for (int kt = 0; kt < kBlock / 32; ++kt)      // four independent accumulators in turn
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1][kt], qb[st], sacc[kt], 0, 0, 0);
+        }
+        // pin the order: the first step's reads, then per step the next step's 4 reads before its 4 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int st = 0; st < kD / 16; ++st) {
+            if (st + 1 < kD / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         __syncthreads();                               // every wave is done with K_n
         if (more) issue_k(kept[n + 1]);
@@ -406,21 +436,34 @@ __device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* 
         if (more) wait_vmcnt<kLoadsPerWave>();         // V_n landed; K_{n+1} may be in flight
         else wait_vmcnt<0>();
         __syncthreads();
+        // the next key step's four V^T fragments are read while this step's four MFMAs run
+        bf16x4 va[2][kD / 32][2];
+#pragma unroll
+        for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                va[0][t][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(v_lds + voff[hh][t]));
 #pragma unroll
         for (int s = 0; s < kBlock / 16; ++s) {
+            if (s + 1 < kBlock / 16) {
+#pragma unroll
+                for (int t = 0; t < kD / 32; ++t)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        va[(s + 1) & 1][t][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (lds_bf16x4*)(v_lds + voff[hh][t] + 16 * (s + 1) * kRowBytes));
+            }
 #pragma unroll
             for (int t = 0; t < kD / 32; ++t) {              // four independent accumulators in turn
-                bf16x4 half[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int r = 16 * s + 8 * g + 4 * hh + jl / 4;
-                    const int c = 4 * t + 2 * (grp % 2) + (jl % 4) / 2;
-                    const uint8_t* p = v_lds + r * kRowBytes + ((c ^ swz(r)) * 16) + 8 * (jl % 2);
-                    half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-                }
-                const bf16x8 a = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8 a = __builtin_shufflevector(va[s & 1][t][0], va[s & 1][t][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], oacc[t], 0, 0, 0);
             }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+        for (int s = 0; s < kBlock / 16; ++s) {
+            if (s + 1 < kBlock / 16) __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
         }
         __syncthreads();                               // every wave is done with V_n
         if (more) issue_v(kept[n + 1]);
