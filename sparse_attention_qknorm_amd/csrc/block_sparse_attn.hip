@@ -281,6 +281,8 @@ constexpr int kRowBytes = kD * 2;
 constexpr int kTileBytes = kBlock * kRowBytes;               // 32 KB
 constexpr int kLoadsPerWave = kTileBytes / 1024 / (kThreads / kWave);   // 8 x 1 KB per wave per tile
 constexpr float kLazyRescale = 8.0f;                         // log2 units
+constexpr int kXcdPeriod = 16;                               // query-block deal over the XCDs: runs of
+constexpr int kXcdRun = 2;                                   // kXcdRun blocks, period kXcdPeriod = 8 runs
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -565,13 +567,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(
     __shared__ uint16_t kept[kMaxBlocks];
     __shared__ int n_kept_s;
 
-    // Hardware deals workgroup ids round-robin over the 8 XCDs. Give XCD x the query
-    // blocks [x*per, (x+1)*per) of every (b, h) in turn, so at any moment all XCDs work on
-    // the same head (one head's K and V stay resident in the memory-side cache) and each
-    // XCD's L2 serves adjacent query blocks, whose kept key blocks overlap.
-    const int per = (nB + kNumXcd - 1) / kNumXcd;
+    // Hardware deals workgroup ids round-robin over the 8 XCDs. All XCDs work on one
+    // (b, h) at a time, so that head's K and V stay resident in the memory-side cache.
+    // Within it, XCD x takes the query blocks i with (i mod kXcdPeriod) / kXcdRun == x in
+    // ascending order: runs of two adjacent blocks dealt round-robin. Measured against
+    // giving each XCD one contiguous range of the head, this is 1.5% faster at the full
+    // layer with bit-identical outputs (a replay of the kept lists through a 4 MB LRU per
+    // XCD puts the L2 hit rate at 56-59% against 42-48%).
+    const int per = (nB + kXcdPeriod - 1) / kXcdPeriod * kXcdRun;
     const int64_t slot = blockIdx.x / kNumXcd;
-    const int i = (int)(blockIdx.x % kNumXcd) * per + (int)(slot % per);
+    const int run = (int)(slot % per);
+    const int i = (run / kXcdRun) * kXcdPeriod + (int)(blockIdx.x % kNumXcd) * kXcdRun + run % kXcdRun;
     if (i >= nB) return;                               // ragged split: whole workgroup leaves
     const int64_t bh = slot / per;
     const int h = (int)(bh % H);
@@ -650,7 +656,7 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const uint8_t* 
                     float scale, void* o, const SelectArgs& sel, hipStream_t stream) {
     const int32_t nB = (S + kBlock - 1) / kBlock;
     const int64_t n_items = (int64_t)B * H * nB;
-    const int per = (nB + kNumXcd - 1) / kNumXcd;
+    const int per = (nB + kXcdPeriod - 1) / kXcdPeriod * kXcdRun;
     const int64_t n_groups = (int64_t)B * H * per * kNumXcd;
     const float scale_log2 = scale * 1.4426950408889634f;
     // bytes of one head's rows within one batch entry, up to the end of row S-1
