@@ -16,30 +16,26 @@
 //             fp64 and the result does not depend on the reduction order.
 //             HBM-bound: 4*D bytes per (token, head).
 //  2. nB <= 1024 (every shape of the layer up to 131,072 tokens at block 128):
-//     transpose: the pooled k means go to [b,h][d][nBpad] (zeros past nB), so
-//             a wavefront reading one d of 256 consecutive key blocks reads
-//             2 KB of contiguous memory.
-//     select_fused: one workgroup per (b, h, strip of 16/32/64 query rows)
-//             computes the strip's scores against every key block in fp64
-//             vector ALU (16 rows x 4 keys per thread; query means broadcast
-//             from LDS, key means straight from the transposed copy), keeps
-//             the upper 32 bits of each score's order key in LDS, and then
-//             each wavefront selects its rows there: a bitwise search over the
-//             32-bit keys, counting with wave ballots, finds the upper half T
-//             of the (k-1)-th largest key; keys above T are kept; when keys
-//             sharing T must be split, only those scores are recomputed in
-//             full (same canonical order) and the search goes on over their
-//             lower 32 bits, ties going to the lower j. The mask row is
-//             written straight from the ballots; nothing of size nB^2 goes
-//             through memory except the mask itself.
+//     limbs:  each pooled vector, scaled by a power of two, is split into three
+//             int8 limbs (exact to 2^-23 of its scale) plus its exponent.
+//     select_filtered: one workgroup per (b, h, strip of 32-128 query rows).
+//             Exact integer MFMAs over the limbs give every score of the strip
+//             to within a proven bound; they are kept as 32-bit fixed-point keys
+//             in LDS. Each wavefront then selects its rows there: a bitwise
+//             search (wave ballots) finds the threshold key to within 1024
+//             units; keys clear of the threshold by more than the bound are
+//             decided by it, and only the few keys inside that band get their
+//             canonical fp64 scores computed, which decide them exactly (ties
+//             to the lower j). The mask row is written from the ballots;
+//             nothing of size nB^2 goes through memory except the mask itself.
 //  3. nB > 1024 (up to 4096):
 //     scores: per (b, h) a tiled nB x nB product of the pooled vectors in fp64
 //             vector ALU (128x128 tile per workgroup, 8x8 per thread, pooled
 //             vectors staged in LDS by 16-wide d slices). The scores leave as
 //             uint64 keys whose unsigned order is the fp64 order.
 //     topk:   one wavefront per query-block row; the row's keys sit in
-//             registers; the same bitwise search (32 steps on the upper halves,
-//             32 more only when keys tie there).
+//             registers; a bitwise search with wave ballots (32 steps on the
+//             upper halves, 32 more only when keys tie there).
 // Contraction into FMA is switched off in every score loop, so each product and
 // each sum rounds on its own, in the order of the definition, and every path
 // produces the same scores bit for bit.
@@ -289,42 +285,93 @@ void launch_topk(const uint64_t* keys, uint8_t* mask, int32_t nB, int64_t rows, 
     hipLaunchKernelGGL((topk_kernel<R>), grid, dim3(kThreads), 0, stream, keys, mask, nB, rows, kept, gate);
 }
 
-// ---------------------------------------------------------------- fused scores + top-k (nB <= 1024)
+// ---------------------------------------------------------------- filtered selection (nB <= 1024)
 
 constexpr int kFusedMaxBlocks = 1024;
 
 __host__ __device__ constexpr int fused_pad(int nB) { return nB <= 256 ? 256 : nB <= 512 ? 512 : 1024; }
 
-// pk [bh][nB][D] -> pkT [bh][D][nBpad], zeros for j >= nB. 32 x 32 tiles of doubles through LDS.
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLimbs = 3;
+constexpr int kNoExp = -4096;             // exponent recorded for an all-zero vector
+constexpr int kKeyFracBits = 27;          // approximate key = floor(score * 2^27) + 2^31
+constexpr int kSearchLowBit = 10;         // the threshold search resolves key bits 31..10
+// Twice the bound on |approximate - exact| score, in key units, rounded up (the bound is
+// derived above select_filtered_kernel): 2 * (2^-16 + 2^-24) * 2^27 < 4112.
+constexpr uint32_t kBand = 4112;
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+// pooled [2][BH][nB][D] fp64 -> limbs [2][BH][3][nBpad][D] int8 (zeros for j >= nB) and, for the k
+// means, exponents [BH][nBpad]. A vector x with max |x_d| = f 2^F (f in [1/2, 1)) is scaled to
+// x~ = x 2^-(F+2), so |x~_d| < 1/4, and written as x~ = a1 2^-8 + a2 2^-15 + a3 2^-22 + r: each a_n
+// rounds what is left to the nearest integer (|a_n| <= 64) and |r| <= 2^-23. Every step is exact
+// in fp64.
 template <int D>
-__global__ __launch_bounds__(kThreads) void transpose_pk_kernel(const double* __restrict__ pk,
-                                                                double* __restrict__ pkT, int32_t nB,
-                                                                int32_t nBpad, const double* __restrict__ gate) {
-    __shared__ double tile[32][33];
+__global__ __launch_bounds__(kThreads) void limbs_kernel(const double* __restrict__ pooled, int8_t* __restrict__ limbs,
+                                                         int32_t* __restrict__ kexp, int64_t BH, int32_t nB,
+                                                         int32_t nBpad, const double* __restrict__ gate) {
+    constexpr int kPer = 16;                             // elements per thread
+    constexpr int kTpr = D / kPer;                       // threads per vector
+    constexpr int kRowsPerWg = kThreads / kTpr;
     if (gate != nullptr && *gate == 0.0) return;
-    constexpr int kDTiles = D / 32;
-    const int jtiles = nBpad / 32;
-    const int64_t bh = blockIdx.x / ((int64_t)jtiles * kDTiles);
-    const int rem = (int)(blockIdx.x % ((int64_t)jtiles * kDTiles));
-    const int j0 = (rem / kDTiles) * 32;
-    const int d0 = (rem % kDTiles) * 32;
-    const int tx = threadIdx.x % 32;
-    const int ty = threadIdx.x / 32;
-    const double* src = pk + bh * (int64_t)nB * D;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerWg + threadIdx.x / kTpr;   // (tensor * BH + bh) * nBpad + j
+    const int part = threadIdx.x % kTpr;
+    const int64_t tbh = row / nBpad;
+    const int j = (int)(row % nBpad);
+
+    double x[kPer];
+    if (j < nB) {
+        const double2* src = (const double2*)(pooled + (tbh * nB + j) * (int64_t)D + part * kPer);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int j = j0 + ty + 8 * r;
-        tile[ty + 8 * r][tx] = j < nB ? src[(int64_t)j * D + d0 + tx] : 0.0;
+        for (int e = 0; e < kPer / 2; ++e) {
+            const double2 v = src[e];
+            x[2 * e] = v.x;
+            x[2 * e + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) x[e] = 0.0;
     }
-    __syncthreads();
-    double* dst = pkT + bh * (int64_t)D * nBpad;
+    double mx = 0.0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(int64_t)(d0 + ty + 8 * r) * nBpad + j0 + tx] = tile[tx][ty + 8 * r];
+    for (int e = 0; e < kPer; ++e) mx = fmax(mx, fabs(x[e]));
+#pragma unroll
+    for (int o = 1; o < kTpr; o <<= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    int F = kNoExp;
+    if (mx > 0.0) (void)frexp(mx, &F);
+    const int up = mx > 0.0 ? 6 - F : 0;                 // y = x~ * 2^8 = x * 2^(6-F)
+
+    uint32_t w[kLimbs][kPer / 4];
+#pragma unroll
+    for (int n = 0; n < kLimbs; ++n)
+#pragma unroll
+        for (int c = 0; c < kPer / 4; ++c) w[n][c] = 0u;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        double y = ldexp(x[e], up);
+        const double a1 = rint(y);
+        y = (y - a1) * 128.0;
+        const double a2 = rint(y);
+        y = (y - a2) * 128.0;
+        const double a3 = rint(y);
+        const int sh = 8 * (e % 4);
+        w[0][e / 4] |= ((uint32_t)(int)a1 & 0xffu) << sh;
+        w[1][e / 4] |= ((uint32_t)(int)a2 & 0xffu) << sh;
+        w[2][e / 4] |= ((uint32_t)(int)a3 & 0xffu) << sh;
+    }
+#pragma unroll
+    for (int n = 0; n < kLimbs; ++n) {
+        int8_t* dst = limbs + ((tbh * kLimbs + n) * nBpad + j) * (int64_t)D + part * kPer;
+        *(uint4*)dst = make_uint4(w[n][0], w[n][1], w[n][2], w[n][3]);
+    }
+    if (tbh >= BH && part == 0) kexp[(tbh - BH) * nBpad + j] = F;
 }
 
-// Exact fp64 score of (query mean x in LDS, key mean y in memory) in the canonical order.
+// Exact fp64 score in the canonical order (both means in memory; x is the same for every lane).
 template <int D>
-__device__ __forceinline__ double canonical_score(const double* x, const double* __restrict__ y) {
+__device__ __noinline__ double canonical_score(const double* __restrict__ x, const double* __restrict__ y) {
 #pragma clang fp contract(off)
     double s = 0.0;
     for (int d = 0; d < D; ++d) {
@@ -334,22 +381,38 @@ __device__ __forceinline__ double canonical_score(const double* x, const double*
     return s;
 }
 
-// Workgroup of 4 wavefronts; WR row groups of 16 query rows x (4 / WR) key groups of 256 key blocks.
-// Lane l of a wavefront holds 16 rows x key blocks 256*kg + 4l .. 4l+3.
-template <int D, int WR>
-__global__ __launch_bounds__(kThreads, WR == 1 ? 2 : 1) void select_fused_kernel(const double* __restrict__ pq,
-                                                                   const double* __restrict__ pk,
-                                                                   const double* __restrict__ pkT,
-                                                                   uint8_t* __restrict__ mask, int32_t nB,
-                                                                   int32_t kept, const double* __restrict__ gate) {
-#pragma clang fp contract(off)
-    constexpr int WK = 4 / WR;
-    constexpr int kRows = 16 * WR;
-    constexpr int kPad = 256 * WK;                       // key columns held (nBpad)
+// One workgroup of 8 wavefronts per (b, h, strip of 32 * 8/KG query rows); nBpad = 128 * KG.
+//
+// Approximate scores. With the limbs above, P_nm = sum_d a_n[d] b_m[d] is an exact integer
+// (v_mfma_i32_16x16x64_i8), and t = P_11 2^-16 + (P_12 + P_21) 2^-23 + (P_13 + P_22 + P_31) 2^-30
+// is exact in fp64. Against x~ . y~ it leaves out the products of order 2^-37 and beyond and the
+// remainders r: per d at most 2 * 64 * 64 * 2^-37 + 64 * 64 * 2^-44 + 2 * 2^-23 / 4 < 2^-23 + 2^-32,
+// so |t - x~ . y~| < 2^-16 + 2^-25 over 128 d. In the head's frame (each key's t times
+// 2^(F_j - Fmax), Fmax the largest key exponent of the head, a power of two <= 1 that keeps the
+// order of every row) the key floor(t 2^(F_j - Fmax + 27)) + 2^31 is off the exact canonical fp64
+// score (same frame; its rounding is below 128 * 2^-53 * 8 = 2^-43) by less than 2^-16 + 2^-24
+// over 2^-27 units: at most kBand / 2.
+//
+// Selection per row. A bitwise search over the keys' upper 22 bits (wave ballots) puts the
+// (k-1)-th largest key K* in [T, T + 1023]; the (k-1)-th largest exact score then lies within
+// kBand / 2 of K*. Keys above T + 1023 + kBand are therefore strictly above it (kept), keys below
+// T - kBand strictly below it (dropped), whatever the ties. The keys left in the band number at
+// least the picks still owed; when they number more, only their canonical fp64 scores are
+// computed and the owed picks go to the largest, ties to the lower j (-0.0 equal to +0.0).
+template <int D, int KG>
+__global__ __launch_bounds__(kSelThreads, 1) void select_filtered_kernel(
+    const double* __restrict__ pq, const double* __restrict__ pk, const int8_t* __restrict__ limbs,
+    const int32_t* __restrict__ kexp, uint8_t* __restrict__ mask, int32_t nB, int32_t kept, int64_t BH,
+    const double* __restrict__ gate) {
+    constexpr int kPad = 128 * KG;                       // key columns held
+    constexpr int kRows = 32 * (kSelWaves / KG);         // query rows per workgroup
+    constexpr int kChunks = D / 64;
     constexpr int kM = kPad / kWave;                     // keys per lane in the selection
-    __shared__ __attribute__((aligned(16))) double xq[kRows * D];
-    __shared__ __attribute__((aligned(16))) uint32_t keys[kRows * kPad];
-    if (gate != nullptr && *gate == 0.0) return;        // the mask of an earlier step is kept
+    __shared__ uint32_t keys[kRows * kPad];              // 128 KB
+    __shared__ int amb_j[kSelWaves][kWave];
+    __shared__ int amb_pick[kSelWaves][kWave];
+    __shared__ int fmax_w[kSelWaves];
+    if (gate != nullptr && *gate == 0.0) return;         // the mask of an earlier step is kept
 
     const int strips = (nB + kRows - 1) / kRows;
     const int64_t bh = blockIdx.x / strips;
@@ -357,172 +420,229 @@ __global__ __launch_bounds__(kThreads, WR == 1 ? 2 : 1) void select_fused_kernel
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
+    const int32_t* ke = kexp + bh * kPad;
 
-    // the strip's query means (zeros past nB)
+    // the head's largest key exponent
     {
-        const double2* src = (const double2*)(pq + (bh * nB + i0) * (int64_t)D);
-        double2* dst = (double2*)xq;
-        const int valid = min(kRows, nB - i0) * D / 2;
-        for (int e = tid; e < kRows * D / 2; e += kThreads) dst[e] = e < valid ? src[e] : make_double2(0.0, 0.0);
+        int f = kNoExp;
+        for (int j = tid; j < nB; j += kSelThreads) f = max(f, ke[j]);
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) f = max(f, __shfl_xor(f, o));
+        if (lane == 0) fmax_w[wave] = f;
     }
     __syncthreads();
+    int fmax = fmax_w[0];
+#pragma unroll
+    for (int w = 1; w < kSelWaves; ++w) fmax = max(fmax, fmax_w[w]);
 
-    // ---- scores: 16 rows x 4 key blocks per lane, d ascending, no FMA
+    // ---- approximate keys: wavefront = 32 query rows (two 16-row tiles) x 128 key blocks
     {
-        const int rg = wave / WK;
-        const int kg = wave % WK;
-        const int jb = 256 * kg + 4 * lane;
-        const double* yp = pkT + bh * (int64_t)D * kPad + jb;
-        const double* xr = xq + 16 * rg * D;
-        double acc[16][4];
+        const int p = wave / KG;
+        const int kg = wave % KG;
+        const int lr = lane % 16;
+        const int lg = lane / 16;
+        const int8_t* ql = limbs + bh * kLimbs * (int64_t)kPad * D;
+        const int8_t* kl = limbs + (BH + bh) * kLimbs * (int64_t)kPad * D;
+        int32x4 qa[2][kLimbs][kChunks];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[r][e] = 0.0;
-        double2 ya[2][2], yb[2][2];                      // [d of the pair][key pair]
-        auto load_y = [&](int d, double2 (&y)[2][2]) {
+            for (int a = 0; a < kLimbs; ++a)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                y[u][0] = *(const double2*)(yp + (int64_t)(d + u) * kPad);
-                y[u][1] = *(const double2*)(yp + (int64_t)(d + u) * kPad + 2);
-            }
+                for (int c = 0; c < kChunks; ++c)
+                    qa[u][a][c] = *(const int32x4*)(ql + ((int64_t)a * kPad + i0 + 32 * p + 16 * u + lr) * D +
+                                                    64 * c + 16 * lg);
+        auto load_k = [&](int t, int32x4 (&kb)[kLimbs][kChunks]) {
+            const int j = 128 * kg + 16 * t + lr;
+#pragma unroll
+            for (int a = 0; a < kLimbs; ++a)
+#pragma unroll
+                for (int c = 0; c < kChunks; ++c)
+                    kb[a][c] = *(const int32x4*)(kl + ((int64_t)a * kPad + j) * D + 64 * c + 16 * lg);
         };
-        auto fma_free = [&](int d, const double2 (&y)[2][2]) {
+        auto tile = [&](int t, const int32x4 (&kb)[kLimbs][kChunks]) {
+            int32x4 g[2][3];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const double2 x = *(const double2*)(xr + r * D + d);    // LDS broadcast: x[r][d], x[r][d+1]
-                const double yv0[4] = {y[0][0].x, y[0][0].y, y[0][1].x, y[0][1].y};
-                const double yv1[4] = {y[1][0].x, y[1][0].y, y[1][1].x, y[1][1].y};
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const double p0 = x.x * yv0[e];
-                    acc[r][e] = acc[r][e] + p0;
-                    const double p1 = x.y * yv1[e];
-                    acc[r][e] = acc[r][e] + p1;
+                for (int n = 0; n < 3; ++n) g[u][n] = int32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    g[u][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[0][c], g[u][0], 0, 0, 0);
+                    g[u][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[1][c], g[u][1], 0, 0, 0);
+                    g[u][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][1][c], kb[0][c], g[u][1], 0, 0, 0);
+                    g[u][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[2][c], g[u][2], 0, 0, 0);
+                    g[u][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][1][c], kb[1][c], g[u][2], 0, 0, 0);
+                    g[u][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][2][c], kb[0][c], g[u][2], 0, 0, 0);
                 }
-            }
-        };
-        load_y(0, ya);
-        for (int d = 0; d < D; d += 4) {
-            load_y(d + 2, yb);
-            fma_free(d, ya);
-            if (d + 4 < D) load_y(d + 4, ya);
-            fma_free(d + 2, yb);
-        }
+            // output element r of lane l: row 4 * (l / 16) + r of the tile, key column l % 16
+            const int j = 128 * kg + 16 * t + lr;
+            const int sh = max(ke[j] - fmax, -1100) + kKeyFracBits;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            uint4 w;
-            w.x = (uint32_t)(order_key(acc[r][0]) >> 32);
-            w.y = (uint32_t)(order_key(acc[r][1]) >> 32);
-            w.z = (uint32_t)(order_key(acc[r][2]) >> 32);
-            w.w = (uint32_t)(order_key(acc[r][3]) >> 32);
-            *(uint4*)(keys + (16 * rg + r) * kPad + jb) = w;
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const double s = (double)g[u][0][r] * 0x1p-16 + (double)g[u][1][r] * 0x1p-23 +
+                                     (double)g[u][2][r] * 0x1p-30;
+                    const int row = 32 * p + 16 * u + 4 * lg + r;
+                    keys[row * kPad + j] = (uint32_t)(int32_t)floor(ldexp(s, sh)) ^ 0x80000000u;
+                }
+        };
+        int32x4 kb0[kLimbs][kChunks], kb1[kLimbs][kChunks];
+        load_k(0, kb0);
+#pragma unroll 1
+        for (int t = 0; t < 8; t += 2) {
+            load_k(t + 1, kb1);
+            tile(t, kb0);
+            if (t + 2 < 8) load_k(t + 2, kb0);
+            tile(t + 1, kb1);
         }
     }
     __syncthreads();
 
-    // ---- selection: wavefront w takes rows w, w+4, ...
+    // ---- selection: wavefront w takes rows w, w + 8, ...
     const uint64_t below = (1ull << lane) - 1ull;
     const int need = kept - 1;                           // blocks chosen besides the diagonal
-    for (int r = wave; r < kRows; r += 4) {
+    for (int r = wave; r < kRows; r += kSelWaves) {
         const int i = i0 + r;
         if (i >= nB) break;
-        // valid keys are >= 2^20 (finite scores); 0 marks j >= nB and the diagonal
+        // valid keys lie in (2^30, 3 * 2^30); 0 marks j >= nB and the diagonal
         uint32_t key[kM];
 #pragma unroll
         for (int m = 0; m < kM; ++m) {
             const int j = lane + kWave * m;
             key[m] = (j < nB && j != i) ? keys[r * kPad + j] : 0u;
         }
-        uint32_t T = 0xffffffffu;                        // need == 0: nothing passes key >= T + 1
-        bool all_eq = true;                              // every key equal to T is kept
-        uint32_t tied = 0;                               // bit m: key[m] == T and must be split
-        uint32_t lo[kM];
-        uint32_t Tlo = 0;
-        int eq_take = 0;
+        uint32_t pick = 0;                               // bit m: key block lane + 64 m is kept
         if (need > 0) {
-            T = 0;
-            for (int bit = 31; bit >= 0; --bit) {
+            uint32_t T = 0;
+            for (int bit = 31; bit >= kSearchLowBit; --bit) {
                 const uint32_t cand = T | (1u << bit);
                 int cnt = 0;
 #pragma unroll
                 for (int m = 0; m < kM; ++m) cnt += __popcll(__ballot(key[m] >= cand));
                 if (cnt >= need) T = cand;
             }
-            int gt = 0, eq = 0;
+            const uint32_t hi = T + ((1u << kSearchLowBit) - 1u) + kBand;
+            const uint32_t lo = T - kBand;
+            uint32_t band = 0;
+            int n_in = 0, n_band = 0;
 #pragma unroll
             for (int m = 0; m < kM; ++m) {
-                gt += __popcll(__ballot(key[m] > T));
-                eq += __popcll(__ballot(key[m] == T));
+                const bool in = key[m] > hi;
+                const bool b = key[m] != 0u && key[m] >= lo && key[m] <= hi;
+                pick |= (uint32_t)in << m;
+                band |= (uint32_t)b << m;
+                n_in += __popcll(__ballot(in));
+                n_band += __popcll(__ballot(b));
             }
-            const int take = need - gt;                  // 1 <= take <= eq
-            if (take < eq) {
-                // split the keys whose upper halves equal T by their full fp64 scores
-                all_eq = false;
-                const double* pkh = pk + bh * (int64_t)nB * D;
+            const int take = need - n_in;                // 1 <= take <= n_band
+            if (take == n_band) {
+                pick |= band;
+            } else if (n_band <= kWave) {
+                // gather the band's key blocks into one slot per lane, score them exactly, rank
+                int pos[kM];
+                int base = 0;
 #pragma unroll
                 for (int m = 0; m < kM; ++m) {
-                    lo[m] = 0;
-                    if (key[m] == T) {
-                        tied |= 1u << m;
-                        lo[m] = (uint32_t)order_key(canonical_score<D>(xq + r * D, pkh + (int64_t)(lane + kWave * m) * D));
-                    }
+                    const bool b = (band >> m) & 1u;
+                    const uint64_t bits = __ballot(b);
+                    pos[m] = base + __popcll(bits & below);
+                    if (b) amb_j[wave][pos[m]] = lane + kWave * m;
+                    base += __popcll(bits);
                 }
-                // largest Tlo with #(tied keys with lo >= Tlo) >= take (Tlo = 0 always qualifies)
-                for (int bit = 31; bit >= 0; --bit) {
-                    const uint32_t cand = Tlo | (1u << bit);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                const int jj = lane < n_band ? amb_j[wave][lane] : 0;
+                uint64_t ek = 0;
+                if (lane < n_band)
+                    ek = order_key(canonical_score<D>(pq + (bh * nB + i) * (int64_t)D, pk + (bh * nB + jj) * (int64_t)D));
+                int rank = 0;
+                for (int e = 0; e < n_band; ++e) {
+                    const uint32_t elo = __shfl((uint32_t)ek, e);
+                    const uint32_t ehi = __shfl((uint32_t)(ek >> 32), e);
+                    const int ej = __shfl(jj, e);
+                    const uint64_t other = ((uint64_t)ehi << 32) | elo;
+                    rank += (other > ek || (other == ek && ej < jj)) ? 1 : 0;
+                }
+                amb_pick[wave][lane] = (lane < n_band && rank < take) ? 1 : 0;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int m = 0; m < kM; ++m)
+                    if ((band >> m) & 1u) pick |= (uint32_t)(amb_pick[wave][pos[m]] != 0) << m;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            } else {
+                // a wide band (many equal or nearly equal scores): exact keys for the whole band,
+                // a 64-bit bitwise search over them, ties to the lower j
+                const double* xrow = pq + (bh * nB + i) * (int64_t)D;
+                uint64_t ek[kM];
+#pragma unroll
+                for (int m = 0; m < kM; ++m)
+                    ek[m] = ((band >> m) & 1u)
+                                ? order_key(canonical_score<D>(xrow, pk + (bh * nB + lane + kWave * m) * (int64_t)D))
+                                : 0ull;
+                uint64_t T64 = 0;
+                for (int bit = 63; bit >= 0; --bit) {
+                    const uint64_t cand = T64 | (1ull << bit);
                     int cnt = 0;
 #pragma unroll
-                    for (int m = 0; m < kM; ++m) cnt += __popcll(__ballot(((tied >> m) & 1u) && lo[m] >= cand));
-                    if (cnt >= take) Tlo = cand;
+                    for (int m = 0; m < kM; ++m) cnt += __popcll(__ballot(((band >> m) & 1u) && ek[m] >= cand));
+                    if (cnt >= take) T64 = cand;
                 }
-                int gt_lo = 0;
+                int gt = 0;
 #pragma unroll
-                for (int m = 0; m < kM; ++m) gt_lo += __popcll(__ballot(((tied >> m) & 1u) && lo[m] > Tlo));
-                eq_take = take - gt_lo;
+                for (int m = 0; m < kM; ++m) gt += __popcll(__ballot(((band >> m) & 1u) && ek[m] > T64));
+                const int eq_take = take - gt;
+                int taken = 0;
+#pragma unroll
+                for (int m = 0; m < kM; ++m) {
+                    const bool b = (band >> m) & 1u;
+                    const uint64_t eqb = __ballot(b && ek[m] == T64);
+                    const int before = taken + __popcll(eqb & below);
+                    taken += __popcll(eqb);
+                    if (b && (ek[m] > T64 || (ek[m] == T64 && before < eq_take))) pick |= 1u << m;
+                }
             }
         }
         uint8_t* mrow = mask + (bh * nB + i) * (int64_t)nB;
-        int taken = 0;
 #pragma unroll
         for (int m = 0; m < kM; ++m) {
             const int j = lane + kWave * m;
-            bool sel;
-            if (all_eq) {
-                sel = key[m] != 0u && key[m] >= T && need > 0;
-            } else {
-                const bool t = (tied >> m) & 1u;
-                const uint64_t eqb = __ballot(t && lo[m] == Tlo);
-                const int before = taken + __popcll(eqb & below);
-                taken += __popcll(eqb);
-                sel = key[m] > T || (t && (lo[m] > Tlo || (lo[m] == Tlo && before < eq_take)));
-            }
-            if (j < nB) mrow[j] = (uint8_t)((sel || j == i) ? 1 : 0);
+            if (j < nB) mrow[j] = (uint8_t)((((pick >> m) & 1u) != 0u || j == i) ? 1 : 0);
         }
     }
 }
 
+template <int D, int KG>
+void launch_filtered_kg(const double* pq, const double* pk, const int8_t* limbs, const int32_t* kexp,
+                        uint8_t* mask, int64_t BH, int32_t nB, int32_t kept, const double* gate,
+                        hipStream_t stream) {
+    constexpr int kRows = 32 * (kSelWaves / KG);
+    const int64_t strips = (nB + kRows - 1) / kRows;
+    hipLaunchKernelGGL((select_filtered_kernel<D, KG>), dim3((unsigned)(BH * strips)), dim3(kSelThreads), 0, stream,
+                       pq, pk, limbs, kexp, mask, nB, kept, BH, gate);
+}
+
 template <int D>
-hipError_t launch_fused(const double* pq, const double* pk, double* pkT, uint8_t* mask, int32_t B, int32_t H,
-                        int32_t nB, int32_t kept, const double* gate, hipStream_t stream) {
+hipError_t launch_filtered(const double* pq, void* tail, uint8_t* mask, int32_t B, int32_t H, int32_t nB,
+                           int32_t kept, const double* gate, hipStream_t stream) {
     const int nBpad = fused_pad(nB);
     const int64_t BH = (int64_t)B * H;
-    hipLaunchKernelGGL((transpose_pk_kernel<D>), dim3((unsigned)(BH * (nBpad / 32) * (D / 32))), dim3(kThreads), 0,
-                       stream, pk, pkT, nB, nBpad, gate);
+    const double* pk = pq + BH * nB * D;
+    int8_t* limbs = (int8_t*)tail;
+    int32_t* kexp = (int32_t*)(limbs + (size_t)2 * BH * kLimbs * nBpad * D);
+    constexpr int kRowsPerWg = kThreads / (D / 16);      // divides nBpad
+    hipLaunchKernelGGL((limbs_kernel<D>), dim3((unsigned)(2 * BH * nBpad / kRowsPerWg)), dim3(kThreads), 0, stream,
+                       pq, limbs, kexp, BH, nB, nBpad, gate);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int WR = 1024 / nBpad;
-    const int64_t strips = (nB + 16 * WR - 1) / (16 * WR);
-    const dim3 grid((unsigned)(BH * strips));
-    if (WR == 1)
-        hipLaunchKernelGGL((select_fused_kernel<D, 1>), grid, dim3(kThreads), 0, stream, pq, pk, pkT, mask, nB, kept,
-                           gate);
-    else if (WR == 2)
-        hipLaunchKernelGGL((select_fused_kernel<D, 2>), grid, dim3(kThreads), 0, stream, pq, pk, pkT, mask, nB, kept,
-                           gate);
-    else
-        hipLaunchKernelGGL((select_fused_kernel<D, 4>), grid, dim3(kThreads), 0, stream, pq, pk, pkT, mask, nB, kept,
-                           gate);
+    if (nBpad == 256) launch_filtered_kg<D, 2>(pq, pk, limbs, kexp, mask, BH, nB, kept, gate, stream);
+    else if (nBpad == 512) launch_filtered_kg<D, 4>(pq, pk, limbs, kexp, mask, BH, nB, kept, gate, stream);
+    else launch_filtered_kg<D, 8>(pq, pk, limbs, kexp, mask, BH, nB, kept, gate, stream);
     return hipGetLastError();
 }
 
@@ -530,7 +650,8 @@ hipError_t launch_fused(const double* pq, const double* pk, double* pkT, uint8_t
 
 size_t select_workspace_bytes(int64_t B, int64_t H, int64_t nB, int64_t D) {
     const size_t pooled = ((size_t)2 * B * H * nB * D * sizeof(double) + 255) / 256 * 256;
-    // nB <= 1024: the transposed pooled k means [B,H][D][nBpad]; beyond: the uint64 score keys [B,H,nB,nB]
+    // nB <= 1024: int8 limbs [2][B,H][3][nBpad][D] + k exponents [B,H][nBpad] (6D + 4 <= 8D bytes per
+    // padded block and head); beyond: the uint64 score keys [B,H,nB,nB]
     const size_t tail = nB <= kFusedMaxBlocks ? (size_t)B * H * D * fused_pad((int)nB) * sizeof(double)
                                               : (size_t)B * H * nB * nB * sizeof(uint64_t);
     return pooled + tail;
@@ -545,8 +666,8 @@ hipError_t launch_select_from_pooled(int32_t B, int32_t S, int32_t H, int32_t D,
     void* tail = (char*)workspace + pooled_bytes;
 
     if (nB <= kFusedMaxBlocks) {
-        return D == 128 ? launch_fused<128>(pq, pk, (double*)tail, mask, B, H, nB, kept, gate, stream)
-                        : launch_fused<64>(pq, pk, (double*)tail, mask, B, H, nB, kept, gate, stream);
+        return D == 128 ? launch_filtered<128>(pq, tail, mask, B, H, nB, kept, gate, stream)
+                        : launch_filtered<64>(pq, tail, mask, B, H, nB, kept, gate, stream);
     }
     uint64_t* keys = (uint64_t*)tail;
     const int32_t tiles = (nB + kTile2 - 1) / kTile2;

@@ -137,6 +137,46 @@ def test_zero_score_ties():
     log("  zero-score ties (signed-zero inputs), repeated blocks: masks equal the oracle's at keep 0.3/0.5/0.8")
 
 
+def _near_tie_keys(S, H, D, block, seed, scale_period=0):
+    """k: every key block repeats one base block; in two blocks of three one element of one token is moved
+    by one bf16 step, so pooled means differ by 2^-7 of an ulp in one coordinate and most scores of a row
+    fall within a relative 2^-14 of each other. With scale_period p, block j is scaled by 2^(j mod p - 3)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nB = -(-S // block)
+    base = rng.standard_normal((block, H, D)).astype(np.float32)
+    kf = np.tile(base, (nB, 1, 1))[:S]
+    if scale_period:
+        for j in range(nB):
+            kf[j * block:(j + 1) * block] *= 2.0 ** (j % scale_period - 3)
+    kb = torch.from_numpy(kf).to(torch.bfloat16).view(torch.int16).numpy().copy()
+    for j in range(nB):
+        if j % 3 == 0:
+            continue
+        t = j * block + int(rng.integers(0, min(block, S - j * block)))
+        d = int(rng.integers(0, D))
+        kb[t, :, d] += 1 if j % 3 == 1 else -1                 # one step away from zero / towards zero
+    k = torch.from_numpy(kb).view(torch.bfloat16)[None]
+    q = torch.from_numpy(rng.standard_normal((1, S, H, D)).astype(np.float32)).to(torch.bfloat16)
+    return q, k
+
+
+@pytest.mark.parametrize("S,H,D,block,keep,scale_period", [
+    (50 * 128 - 37, 2, 128, 128, 0.3, 0),      # band of up to 49 near-tied keys
+    (200 * 128 - 5, 2, 64, 128, 0.5, 0),       # band wider than a wavefront
+    (120 * 128, 2, 128, 128, 0.2, 5),          # key blocks at five scales: ties within each scale
+    (600 * 64 - 10, 1, 128, 64, 0.15, 3),      # 1024-column strips
+])
+def test_near_tie_scores(S, H, D, block, keep, scale_period):
+    # Rows whose threshold falls among many exactly or nearly equal scores: the selection has to split
+    # them by their exact fp64 scores, ties to the lower j. The mask must be the oracle's, bit for bit.
+    q, k = _near_tie_keys(S, H, D, block, seed=S + D, scale_period=scale_period)
+    mask = saq.select_blocks(q.to(DEV), k.to(DEV), keep, block).cpu().numpy()
+    ref = oracle_mask(to64(q), to64(k), block, keep)
+    for (b, h), m in ref.items():
+        assert np.array_equal(mask[b, h], m), f"mask differs on head {h}"
+    log(f"  near-tie scores S={S} D={D} block={block} keep={keep} scales={scale_period}: masks equal the oracle's")
+
+
 def test_user_mask_with_empty_rows_and_all_ones():
     inp = synth.make_small_case(700, 2, 128, seed=3, sections=(32, 48, 48), T=1, Hg=20, W=30)
     g = _upload(inp)
