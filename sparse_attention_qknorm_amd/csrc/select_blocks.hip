@@ -302,6 +302,7 @@ constexpr int kSearchLowBit = 10;         // the threshold search resolves key b
 constexpr uint32_t kBand = 4112;
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelU = 1;                  // 16-row query tiles per wavefront in the score phase
 
 // pooled [2][BH][nB][D] fp64 -> limbs [2][BH][3][nBpad][D] int8 (zeros for j >= nB) and, for the k
 // means, exponents [BH][nBpad]. A vector x with max |x_d| = f 2^F (f in [1/2, 1)) is scaled to
@@ -369,9 +370,22 @@ __global__ __launch_bounds__(kThreads) void limbs_kernel(const double* __restric
     if (tbh >= BH && part == 0) kexp[(tbh - BH) * nBpad + j] = F;
 }
 
-// Exact fp64 score in the canonical order (both means in memory; x is the same for every lane).
+// Exact fp64 score in the canonical order, both means in LDS.
 template <int D>
-__device__ __noinline__ double canonical_score(const double* __restrict__ x, const double* __restrict__ y) {
+__device__ __forceinline__ double canonical_score_lds(const double* x, const double* y) {
+#pragma clang fp contract(off)
+    double s = 0.0;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) {
+        const double prod = x[d] * y[d];
+        s = s + prod;
+    }
+    return s;
+}
+
+// The same score with the key mean in memory, as a plain call, for the rare wide bands.
+template <int D>
+__device__ __noinline__ double canonical_score_call(const double* x, const double* __restrict__ y) {
 #pragma clang fp contract(off)
     double s = 0.0;
     for (int d = 0; d < D; ++d) {
@@ -381,36 +395,49 @@ __device__ __noinline__ double canonical_score(const double* __restrict__ x, con
     return s;
 }
 
+// wavefront-wide reductions of the device library (DPP lane exchanges)
+extern "C" __device__ int32_t __ockl_wfred_max_i32(int32_t);
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfred_min_u32(uint32_t);
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // One workgroup of 8 wavefronts per (b, h, strip of 32 * 8/KG query rows); nBpad = 128 * KG.
 //
 // Approximate scores. With the limbs above, P_nm = sum_d a_n[d] b_m[d] is an exact integer
-// (v_mfma_i32_16x16x64_i8), and t = P_11 2^-16 + (P_12 + P_21) 2^-23 + (P_13 + P_22 + P_31) 2^-30
-// is exact in fp64. Against x~ . y~ it leaves out the products of order 2^-37 and beyond and the
-// remainders r: per d at most 2 * 64 * 64 * 2^-37 + 64 * 64 * 2^-44 + 2 * 2^-23 / 4 < 2^-23 + 2^-32,
-// so |t - x~ . y~| < 2^-16 + 2^-25 over 128 d. In the head's frame (each key's t times
-// 2^(F_j - Fmax), Fmax the largest key exponent of the head, a power of two <= 1 that keeps the
-// order of every row) the key floor(t 2^(F_j - Fmax + 27)) + 2^31 is off the exact canonical fp64
-// score (same frame; its rounding is below 128 * 2^-53 * 8 = 2^-43) by less than 2^-16 + 2^-24
-// over 2^-27 units: at most kBand / 2.
+// (v_mfma_i32_16x16x64_i8), and so is t 2^30 = P_11 2^14 + (P_12 + P_21) 2^7 + (P_13 + P_22 + P_31).
+// Against x~ . y~, t leaves out the products of order 2^-37 and beyond and the remainders r: per d
+// at most 2 * 64 * 64 * 2^-37 + 64 * 64 * 2^-44 + 2 * 2^-23 / 4 < 2^-23 + 2^-32, so
+// |t - x~ . y~| < 2^-16 + 2^-25 over 128 d. In the head's frame (each key's t times 2^(F_j - Fmax),
+// Fmax the largest key exponent of the head: a power of two <= 1, so every row keeps its order)
+// the key floor(t 2^(F_j - Fmax + 27)) + 2^31, an integer shift of t 2^30, is off the exact
+// canonical fp64 score in the same frame (whose own rounding is below 128 * 2^-53 * 8 = 2^-43) by
+// less than (2^-16 + 2^-24) / 2^-27 units: at most kBand / 2.
 //
-// Selection per row. A bitwise search over the keys' upper 22 bits (wave ballots) puts the
-// (k-1)-th largest key K* in [T, T + 1023]; the (k-1)-th largest exact score then lies within
-// kBand / 2 of K*. Keys above T + 1023 + kBand are therefore strictly above it (kept), keys below
-// T - kBand strictly below it (dropped), whatever the ties. The keys left in the band number at
-// least the picks still owed; when they number more, only their canonical fp64 scores are
-// computed and the owed picks go to the largest, ties to the lower j (-0.0 equal to +0.0).
+// Selection per row. A bitwise search with wave ballots, started below the bits all the row's keys
+// share and narrowed to one key per lane once at most 64 keys remain in play, puts the (k-1)-th
+// largest key K* in [T, T + 1023]; the (k-1)-th largest exact score then lies within kBand / 2 of
+// K*. Keys above T + 1023 + kBand are therefore strictly above it (kept), keys below T - kBand
+// strictly below it (dropped), whatever the ties. The keys left in the band number at least the
+// picks still owed; when they number more, only their canonical fp64 scores are computed and the
+// owed picks go to the largest, ties to the lower j (-0.0 equal to +0.0).
 template <int D, int KG>
-__global__ __launch_bounds__(kSelThreads, 1) void select_filtered_kernel(
+__global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filtered_kernel(
     const double* __restrict__ pq, const double* __restrict__ pk, const int8_t* __restrict__ limbs,
     const int32_t* __restrict__ kexp, uint8_t* __restrict__ mask, int32_t nB, int32_t kept, int64_t BH,
     const double* __restrict__ gate) {
     constexpr int kPad = 128 * KG;                       // key columns held
-    constexpr int kRows = 32 * (kSelWaves / KG);         // query rows per workgroup
+    constexpr int kRows = 16 * kSelU * (kSelWaves / KG); // query rows per workgroup
     constexpr int kChunks = D / 64;
     constexpr int kM = kPad / kWave;                     // keys per lane in the selection
-    __shared__ uint32_t keys[kRows * kPad];              // 128 KB
-    __shared__ int amb_j[kSelWaves][kWave];
-    __shared__ int amb_pick[kSelWaves][kWave];
+    constexpr int kTiles = 8;                            // 16-key tiles per wavefront
+    __shared__ uint32_t keys[kRows * kPad];              // 64 KB per 16-row tile per wavefront
+    __shared__ __attribute__((aligned(16))) double xrow[kSelWaves][D];
+    __shared__ uint32_t slot[kSelWaves][kWave];
+    __shared__ int pick_s[kSelWaves][kWave];
     __shared__ int fmax_w[kSelWaves];
     if (gate != nullptr && *gate == 0.0) return;         // the mask of an earlier step is kept
 
@@ -422,19 +449,6 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_filtered_kernel(
     const int lane = tid % kWave;
     const int32_t* ke = kexp + bh * kPad;
 
-    // the head's largest key exponent
-    {
-        int f = kNoExp;
-        for (int j = tid; j < nB; j += kSelThreads) f = max(f, ke[j]);
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) f = max(f, __shfl_xor(f, o));
-        if (lane == 0) fmax_w[wave] = f;
-    }
-    __syncthreads();
-    int fmax = fmax_w[0];
-#pragma unroll
-    for (int w = 1; w < kSelWaves; ++w) fmax = max(fmax, fmax_w[w]);
-
     // ---- approximate keys: wavefront = 32 query rows (two 16-row tiles) x 128 key blocks
     {
         const int p = wave / KG;
@@ -443,33 +457,52 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_filtered_kernel(
         const int lg = lane / 16;
         const int8_t* ql = limbs + bh * kLimbs * (int64_t)kPad * D;
         const int8_t* kl = limbs + (BH + bh) * kLimbs * (int64_t)kPad * D;
-        int32x4 qa[2][kLimbs][kChunks];
+        // operand loads first; the exponent reduction runs while they are in flight
+        int32x4 qa[kSelU][kLimbs][kChunks];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < kSelU; ++u)
 #pragma unroll
             for (int a = 0; a < kLimbs; ++a)
 #pragma unroll
                 for (int c = 0; c < kChunks; ++c)
-                    qa[u][a][c] = *(const int32x4*)(ql + ((int64_t)a * kPad + i0 + 32 * p + 16 * u + lr) * D +
+                    qa[u][a][c] = *(const int32x4*)(ql + ((int64_t)a * kPad + i0 + 16 * (kSelU * p + u) + lr) * D +
                                                     64 * c + 16 * lg);
-        auto load_k = [&](int t, int32x4 (&kb)[kLimbs][kChunks]) {
+        // a tile's key limbs and exponent are loaded together, one tile ahead of their use
+        auto load_k = [&](int t, int32x4 (&kb)[kLimbs][kChunks], int& f) {
             const int j = 128 * kg + 16 * t + lr;
 #pragma unroll
             for (int a = 0; a < kLimbs; ++a)
 #pragma unroll
                 for (int c = 0; c < kChunks; ++c)
                     kb[a][c] = *(const int32x4*)(kl + ((int64_t)a * kPad + j) * D + 64 * c + 16 * lg);
+            f = ke[j];
         };
-        auto tile = [&](int t, const int32x4 (&kb)[kLimbs][kChunks]) {
-            int32x4 g[2][3];
+        int32x4 kb0[kLimbs][kChunks], kb1[kLimbs][kChunks];
+        int f0, f1;
+        load_k(0, kb0, f0);
+
+        // the head's largest key exponent
+        {
+            int f = kNoExp;
+            for (int j = tid; j < nB; j += kSelThreads) f = max(f, ke[j]);
+            f = __ockl_wfred_max_i32(f);
+            if (lane == 0) fmax_w[wave] = f;
+        }
+        __syncthreads();
+        int fmax = fmax_w[0];
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+        for (int w = 1; w < kSelWaves; ++w) fmax = max(fmax, fmax_w[w]);
+
+        auto tile = [&](int t, const int32x4 (&kb)[kLimbs][kChunks], int fj) {
+            int32x4 g[kSelU][3];
+#pragma unroll
+            for (int u = 0; u < kSelU; ++u)
 #pragma unroll
                 for (int n = 0; n < 3; ++n) g[u][n] = int32x4{0, 0, 0, 0};
 #pragma unroll
             for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < kSelU; ++u) {
                     g[u][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[0][c], g[u][0], 0, 0, 0);
                     g[u][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[1][c], g[u][1], 0, 0, 0);
                     g[u][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][1][c], kb[0][c], g[u][1], 0, 0, 0);
@@ -479,25 +512,22 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_filtered_kernel(
                 }
             // output element r of lane l: row 4 * (l / 16) + r of the tile, key column l % 16
             const int j = 128 * kg + 16 * t + lr;
-            const int sh = max(ke[j] - fmax, -1100) + kKeyFracBits;
+            const int shift = min(fmax - fj + 3, 63);     // >= 3
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < kSelU; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const double s = (double)g[u][0][r] * 0x1p-16 + (double)g[u][1][r] * 0x1p-23 +
-                                     (double)g[u][2][r] * 0x1p-30;
-                    const int row = 32 * p + 16 * u + 4 * lg + r;
-                    keys[row * kPad + j] = (uint32_t)(int32_t)floor(ldexp(s, sh)) ^ 0x80000000u;
+                    const int64_t t30 = ((int64_t)g[u][0][r] << 14) + ((int64_t)g[u][1][r] << 7) + (int64_t)g[u][2][r];
+                    const int row = 16 * (kSelU * p + u) + 4 * lg + r;
+                    keys[row * kPad + j] = (uint32_t)(int32_t)(t30 >> shift) ^ 0x80000000u;
                 }
         };
-        int32x4 kb0[kLimbs][kChunks], kb1[kLimbs][kChunks];
-        load_k(0, kb0);
 #pragma unroll 1
-        for (int t = 0; t < 8; t += 2) {
-            load_k(t + 1, kb1);
-            tile(t, kb0);
-            if (t + 2 < 8) load_k(t + 2, kb0);
-            tile(t + 1, kb1);
+        for (int t = 0; t < kTiles; t += 2) {
+            load_k(t + 1, kb1, f1);
+            tile(t, kb0, f0);
+            if (t + 2 < kTiles) load_k(t + 2, kb0, f0);
+            tile(t + 1, kb1, f1);
         }
     }
     __syncthreads();
@@ -513,17 +543,59 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_filtered_kernel(
 #pragma unroll
         for (int m = 0; m < kM; ++m) {
             const int j = lane + kWave * m;
-            key[m] = (j < nB && j != i) ? keys[r * kPad + j] : 0u;
+            const uint32_t v = keys[r * kPad + j];
+            key[m] = (j < nB && j != i) ? v : 0u;
         }
         uint32_t pick = 0;                               // bit m: key block lane + 64 m is kept
         if (need > 0) {
-            uint32_t T = 0;
-            for (int bit = 31; bit >= kSearchLowBit; --bit) {
+            // bits shared by every valid key of the row
+            uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+            for (int m = 0; m < kM; ++m) {
+                kmax = max(kmax, key[m]);
+                kmin = min(kmin, key[m] != 0u ? key[m] : 0xffffffffu);
+            }
+            kmax = __ockl_wfred_max_u32(kmax);
+            kmin = __ockl_wfred_min_u32(kmin);
+            // invariant: K* lies in [T, T + 2^(bit+1)); cT keys are >= T, cU keys >= T + 2^(bit+1)
+            int bit = 31 - __clz((int)(kmin ^ kmax));     // -1 when all keys are equal
+            uint32_t T = bit >= 31 ? 0u : bit < 0 ? kmin : (kmin & ~((2u << bit) - 1u));
+            int cT = nB - 1, cU = 0;
+            for (; bit >= kSearchLowBit && cT - cU > kWave; --bit) {
                 const uint32_t cand = T | (1u << bit);
+                uint64_t bl[kM];
+#pragma unroll
+                for (int m = 0; m < kM; ++m) bl[m] = __ballot(key[m] >= cand);
                 int cnt = 0;
 #pragma unroll
-                for (int m = 0; m < kM; ++m) cnt += __popcll(__ballot(key[m] >= cand));
-                if (cnt >= need) T = cand;
+                for (int m = 0; m < kM; ++m) cnt += __popcll(bl[m]);
+                if (cnt >= need) {
+                    T = cand;
+                    cT = cnt;
+                } else {
+                    cU = cnt;
+                }
+            }
+            if (bit >= kSearchLowBit) {
+                // at most 64 keys in [T, T + 2^(bit+1)): one per lane for the remaining bits
+                const uint32_t width = bit >= 31 ? 0xffffffffu : (2u << bit) - 1u;
+                int base = 0;
+#pragma unroll
+                for (int m = 0; m < kM; ++m) {
+                    const bool in = key[m] != 0u && key[m] >= T && key[m] - T <= width;
+                    const uint64_t bits = __ballot(in);
+                    const int at = base + __popcll(bits & below);
+                    if (in && at < kWave) slot[wave][at] = key[m];
+                    base += __popcll(bits);
+                }
+                wave_sync_lds();
+                const uint32_t ck = lane < base ? slot[wave][lane] : 0u;
+                wave_sync_lds();
+                const int above = cU;                    // keys above the gathered range
+                for (; bit >= kSearchLowBit; --bit) {
+                    const uint32_t cand = T | (1u << bit);
+                    if (above + __popcll(__ballot(ck >= cand)) >= need) T = cand;
+                }
             }
             const uint32_t hi = T + ((1u << kSearchLowBit) - 1u) + kBand;
             const uint32_t lo = T - kBand;
@@ -541,71 +613,101 @@ __global__ __launch_bounds__(kSelThreads, 1) void select_filtered_kernel(
             const int take = need - n_in;                // 1 <= take <= n_band
             if (take == n_band) {
                 pick |= band;
-            } else if (n_band <= kWave) {
-                // gather the band's key blocks into one slot per lane, score them exactly, rank
-                int pos[kM];
-                int base = 0;
-#pragma unroll
-                for (int m = 0; m < kM; ++m) {
-                    const bool b = (band >> m) & 1u;
-                    const uint64_t bits = __ballot(b);
-                    pos[m] = base + __popcll(bits & below);
-                    if (b) amb_j[wave][pos[m]] = lane + kWave * m;
-                    base += __popcll(bits);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                const int jj = lane < n_band ? amb_j[wave][lane] : 0;
-                uint64_t ek = 0;
-                if (lane < n_band)
-                    ek = order_key(canonical_score<D>(pq + (bh * nB + i) * (int64_t)D, pk + (bh * nB + jj) * (int64_t)D));
-                int rank = 0;
-                for (int e = 0; e < n_band; ++e) {
-                    const uint32_t elo = __shfl((uint32_t)ek, e);
-                    const uint32_t ehi = __shfl((uint32_t)(ek >> 32), e);
-                    const int ej = __shfl(jj, e);
-                    const uint64_t other = ((uint64_t)ehi << 32) | elo;
-                    rank += (other > ek || (other == ek && ej < jj)) ? 1 : 0;
-                }
-                amb_pick[wave][lane] = (lane < n_band && rank < take) ? 1 : 0;
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int m = 0; m < kM; ++m)
-                    if ((band >> m) & 1u) pick |= (uint32_t)(amb_pick[wave][pos[m]] != 0) << m;
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
             } else {
-                // a wide band (many equal or nearly equal scores): exact keys for the whole band,
-                // a 64-bit bitwise search over them, ties to the lower j
-                const double* xrow = pq + (bh * nB + i) * (int64_t)D;
-                uint64_t ek[kM];
+                const double* xg = pq + (bh * nB + i) * (int64_t)D;     // the row's query mean
+                const double* pkh = pk + bh * nB * (int64_t)D;
+                if (n_band <= kWave) {
+                    // gather the band's key blocks into one slot per lane, score them exactly, rank
+                    int base = 0;
 #pragma unroll
-                for (int m = 0; m < kM; ++m)
-                    ek[m] = ((band >> m) & 1u)
-                                ? order_key(canonical_score<D>(xrow, pk + (bh * nB + lane + kWave * m) * (int64_t)D))
-                                : 0ull;
-                uint64_t T64 = 0;
-                for (int bit = 63; bit >= 0; --bit) {
-                    const uint64_t cand = T64 | (1ull << bit);
-                    int cnt = 0;
+                    for (int m = 0; m < kM; ++m) {
+                        const bool b = (band >> m) & 1u;
+                        const uint64_t bits = __ballot(b);
+                        const int at = base + __popcll(bits & below);
+                        if (b && at < kWave) slot[wave][at] = (uint32_t)(lane + kWave * m);
+                        base += __popcll(bits);
+                    }
+                    wave_sync_lds();
+                    const int jj = lane < n_band ? (int)slot[wave][lane] : 0;
+                    // The query mean goes to xrow, the band's key means kStage at a time to this row's
+                    // key region (its keys are in registers by now); every load of a round is issued
+                    // before the first store, then lane e scores band entry e from LDS.
+                    constexpr int kStage = kPad * 4 / (D * 8);
+                    double* ybuf = (double*)&keys[r * kPad];
+                    const bool xl = 2 * lane < D;
+                    double2 xv = make_double2(0.0, 0.0);
+                    if (xl) xv = *(const double2*)(xg + 2 * lane);
+                    uint64_t ek = 0;
+                    for (int g0 = 0; g0 < n_band; g0 += kStage) {
+                        const int cnt = min(kStage, n_band - g0);
+                        double2 yv[kStage];
 #pragma unroll
-                    for (int m = 0; m < kM; ++m) cnt += __popcll(__ballot(((band >> m) & 1u) && ek[m] >= cand));
-                    if (cnt >= take) T64 = cand;
+                        for (int s2 = 0; s2 < kStage; ++s2) {
+                            const int js = __shfl(jj, min(g0 + s2, n_band - 1));    // past the band: a repeat
+                            yv[s2] = xl ? *(const double2*)(pkh + (int64_t)js * D + 2 * lane) : make_double2(0.0, 0.0);
+                        }
+                        if (g0 == 0 && xl) *(double2*)&xrow[wave][2 * lane] = xv;
+#pragma unroll
+                        for (int s2 = 0; s2 < kStage; ++s2)
+                            if (s2 < cnt && xl) *(double2*)&ybuf[s2 * D + 2 * lane] = yv[s2];
+                        wave_sync_lds();
+                        if (lane >= g0 && lane < g0 + cnt)
+                            ek = order_key(canonical_score_lds<D>(xrow[wave], ybuf + (lane - g0) * D));
+                        wave_sync_lds();
+                    }
+                    int rank = 0;
+                    for (int e = 0; e < n_band; ++e) {
+                        const uint32_t elo = __shfl((uint32_t)ek, e);
+                        const uint32_t ehi = __shfl((uint32_t)(ek >> 32), e);
+                        const int ej = __shfl(jj, e);
+                        const uint64_t other = ((uint64_t)ehi << 32) | elo;
+                        rank += (other > ek || (other == ek && ej < jj)) ? 1 : 0;
+                    }
+                    pick_s[wave][lane] = (lane < n_band && rank < take) ? 1 : 0;
+                    wave_sync_lds();
+                    base = 0;
+#pragma unroll
+                    for (int m = 0; m < kM; ++m) {
+                        const bool b = (band >> m) & 1u;
+                        const uint64_t bits = __ballot(b);
+                        const int at = base + __popcll(bits & below);
+                        if (b && at < kWave) pick |= (uint32_t)(pick_s[wave][at] != 0) << m;
+                        base += __popcll(bits);
+                    }
+                } else {
+                    // a wide band (many equal or nearly equal scores): exact keys for the whole band,
+                    // a 64-bit bitwise search over them, ties to the lower j
+                    for (int d = 2 * lane; d < D; d += 2 * kWave) *(double2*)&xrow[wave][d] = *(const double2*)(xg + d);
+                    wave_sync_lds();
+                    uint64_t ek[kM];
+#pragma unroll
+                    for (int m = 0; m < kM; ++m)
+                        ek[m] = ((band >> m) & 1u)
+                                    ? order_key(canonical_score_call<D>(xrow[wave], pkh + (int64_t)(lane + kWave * m) * D))
+                                    : 0ull;
+                    uint64_t T64 = 0;
+                    for (int b64 = 63; b64 >= 0; --b64) {
+                        const uint64_t cand = T64 | (1ull << b64);
+                        int cnt = 0;
+#pragma unroll
+                        for (int m = 0; m < kM; ++m) cnt += __popcll(__ballot(((band >> m) & 1u) && ek[m] >= cand));
+                        if (cnt >= take) T64 = cand;
+                    }
+                    int gt = 0;
+#pragma unroll
+                    for (int m = 0; m < kM; ++m) gt += __popcll(__ballot(((band >> m) & 1u) && ek[m] > T64));
+                    const int eq_take = take - gt;
+                    int taken = 0;
+#pragma unroll
+                    for (int m = 0; m < kM; ++m) {
+                        const bool b = (band >> m) & 1u;
+                        const uint64_t eqb = __ballot(b && ek[m] == T64);
+                        const int before = taken + __popcll(eqb & below);
+                        taken += __popcll(eqb);
+                        if (b && (ek[m] > T64 || (ek[m] == T64 && before < eq_take))) pick |= 1u << m;
+                    }
                 }
-                int gt = 0;
-#pragma unroll
-                for (int m = 0; m < kM; ++m) gt += __popcll(__ballot(((band >> m) & 1u) && ek[m] > T64));
-                const int eq_take = take - gt;
-                int taken = 0;
-#pragma unroll
-                for (int m = 0; m < kM; ++m) {
-                    const bool b = (band >> m) & 1u;
-                    const uint64_t eqb = __ballot(b && ek[m] == T64);
-                    const int before = taken + __popcll(eqb & below);
-                    taken += __popcll(eqb);
-                    if (b && (ek[m] > T64 || (ek[m] == T64 && before < eq_take))) pick |= 1u << m;
-                }
+                wave_sync_lds();
             }
         }
         uint8_t* mrow = mask + (bh * nB + i) * (int64_t)nB;
@@ -621,7 +723,7 @@ template <int D, int KG>
 void launch_filtered_kg(const double* pq, const double* pk, const int8_t* limbs, const int32_t* kexp,
                         uint8_t* mask, int64_t BH, int32_t nB, int32_t kept, const double* gate,
                         hipStream_t stream) {
-    constexpr int kRows = 32 * (kSelWaves / KG);
+    constexpr int kRows = 16 * kSelU * (kSelWaves / KG);
     const int64_t strips = (nB + kRows - 1) / kRows;
     hipLaunchKernelGGL((select_filtered_kernel<D, KG>), dim3((unsigned)(BH * strips)), dim3(kSelThreads), 0, stream,
                        pq, pk, limbs, kexp, mask, nB, kept, BH, gate);
