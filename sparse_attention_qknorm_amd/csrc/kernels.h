@@ -25,9 +25,9 @@ hipError_t launch_qknorm_rope(const void* q_in, const void* k_in, void* q_out, v
 
 // Workspace layout of the selection: pooled fp64 vectors of q then k
 // [2][B][H][nB][D] (padded to 256 bytes), then for nB <= 1024 the int8 limbs
-// of both [2][B][H][3][nBpad][D] (nBpad = 256, 512 or 1024) and the k vectors'
-// exponents [B][H][nBpad] (int32) within B*H*D*nBpad*8 bytes, for larger nB the
-// uint64 score keys [B][H][nB][nB].
+// of both [2][B][H][4][D/16][nBpad][16] (nBpad = 256, 512 or 1024) and the k vectors'
+// exponents [B][H][nBpad] (int32), for larger nB the uint64 score keys
+// [B][H][nB][nB].
 size_t select_workspace_bytes(int64_t B, int64_t H, int64_t nB, int64_t D);
 
 hipError_t launch_select_blocks(const void* q, const void* k, int32_t B, int32_t S, int32_t H, int32_t D,

@@ -16,13 +16,13 @@
 //             fp64 and the result does not depend on the reduction order.
 //             HBM-bound: 4*D bytes per (token, head).
 //  2. nB <= 1024 (every shape of the layer up to 131,072 tokens at block 128):
-//     limbs:  each pooled vector, scaled by a power of two, is split into three
-//             int8 limbs (exact to 2^-23 of its scale) plus its exponent.
+//     limbs:  each pooled vector, scaled by a power of two, is split into four
+//             int8 limbs (exact to 2^-30 of its scale) plus its exponent.
 //     select_filtered: one workgroup per (b, h, strip of 32-128 query rows).
 //             Exact integer MFMAs over the limbs give every score of the strip
 //             to within a proven bound; they are kept as 32-bit fixed-point keys
 //             in LDS. Each wavefront then selects its rows there: a bitwise
-//             search (wave ballots) finds the threshold key to within 1024
+//             search (wave ballots) finds the threshold key to within 16
 //             units; keys clear of the threshold by more than the bound are
 //             decided by it, and only the few keys inside that band get their
 //             canonical fp64 scores computed, which decide them exactly (ties
@@ -293,22 +293,23 @@ __host__ __device__ constexpr int fused_pad(int nB) { return nB <= 256 ? 256 : n
 
 typedef int int32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLimbs = 3;
+constexpr int kLimbs = 4;
 constexpr int kNoExp = -4096;             // exponent recorded for an all-zero vector
 constexpr int kKeyFracBits = 27;          // approximate key = floor(score * 2^27) + 2^31
-constexpr int kSearchLowBit = 10;         // the threshold search resolves key bits 31..10
+constexpr int kSearchLowBit = 4;          // the threshold search resolves key bits 31..4
 // Twice the bound on |approximate - exact| score, in key units, rounded up (the bound is
-// derived above select_filtered_kernel): 2 * (2^-16 + 2^-24) * 2^27 < 4112.
-constexpr uint32_t kBand = 4112;
+// derived above select_filtered_kernel): 2 * 1.75 * 2^-23 * 2^27 = 56.
+constexpr uint32_t kBand = 56;
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kSelU = 1;                  // 16-row query tiles per wavefront in the score phase
 
-// pooled [2][BH][nB][D] fp64 -> limbs [2][BH][3][nBpad][D] int8 (zeros for j >= nB) and, for the k
-// means, exponents [BH][nBpad]. A vector x with max |x_d| = f 2^F (f in [1/2, 1)) is scaled to
-// x~ = x 2^-(F+2), so |x~_d| < 1/4, and written as x~ = a1 2^-8 + a2 2^-15 + a3 2^-22 + r: each a_n
-// rounds what is left to the nearest integer (|a_n| <= 64) and |r| <= 2^-23. Every step is exact
-// in fp64.
+// pooled [2][BH][nB][D] fp64 -> limbs [2][BH][4][D/16][nBpad][16] int8 (16-byte pieces of the
+// vectors, piece-major so that 16 consecutive blocks' pieces are 256 contiguous bytes, the shape
+// of one MFMA operand load; zeros for j >= nB) and, for the k means, exponents [BH][nBpad]. A vector x with max |x_d| = f 2^F (f in [1/2, 1)) is scaled to
+// x~ = x 2^-(F+2), so |x~_d| < 1/4, and written as x~ = a1 2^-8 + a2 2^-15 + a3 2^-22 + a4 2^-29 + r:
+// each a_n rounds what is left to the nearest integer (|a_n| <= 64) and |r| <= 2^-30. Every step is
+// exact in fp64.
 template <int D>
 __global__ __launch_bounds__(kThreads) void limbs_kernel(const double* __restrict__ pooled, int8_t* __restrict__ limbs,
                                                          int32_t* __restrict__ kexp, int64_t BH, int32_t nB,
@@ -357,14 +358,17 @@ __global__ __launch_bounds__(kThreads) void limbs_kernel(const double* __restric
         const double a2 = rint(y);
         y = (y - a2) * 128.0;
         const double a3 = rint(y);
+        y = (y - a3) * 128.0;
+        const double a4 = rint(y);
         const int sh = 8 * (e % 4);
         w[0][e / 4] |= ((uint32_t)(int)a1 & 0xffu) << sh;
         w[1][e / 4] |= ((uint32_t)(int)a2 & 0xffu) << sh;
         w[2][e / 4] |= ((uint32_t)(int)a3 & 0xffu) << sh;
+        w[3][e / 4] |= ((uint32_t)(int)a4 & 0xffu) << sh;
     }
 #pragma unroll
     for (int n = 0; n < kLimbs; ++n) {
-        int8_t* dst = limbs + ((tbh * kLimbs + n) * nBpad + j) * (int64_t)D + part * kPer;
+        int8_t* dst = limbs + (((tbh * kLimbs + n) * kTpr + part) * nBpad + j) * (int64_t)kPer;
         *(uint4*)dst = make_uint4(w[n][0], w[n][1], w[n][2], w[n][3]);
     }
     if (tbh >= BH && part == 0) kexp[(tbh - BH) * nBpad + j] = F;
@@ -408,19 +412,20 @@ __device__ __forceinline__ void wave_sync_lds() {
 // One workgroup of 8 wavefronts per (b, h, strip of 32 * 8/KG query rows); nBpad = 128 * KG.
 //
 // Approximate scores. With the limbs above, P_nm = sum_d a_n[d] b_m[d] is an exact integer
-// (v_mfma_i32_16x16x64_i8), and so is t 2^30 = P_11 2^14 + (P_12 + P_21) 2^7 + (P_13 + P_22 + P_31).
-// Against x~ . y~, t leaves out the products of order 2^-37 and beyond and the remainders r: per d
-// at most 2 * 64 * 64 * 2^-37 + 64 * 64 * 2^-44 + 2 * 2^-23 / 4 < 2^-23 + 2^-32, so
-// |t - x~ . y~| < 2^-16 + 2^-25 over 128 d. In the head's frame (each key's t times 2^(F_j - Fmax),
+// (v_mfma_i32_16x16x64_i8), and so is t 2^37 = sum over n + m <= 5 of P_nm 2^(7 (5 - n - m)):
+// ten products, grouped by n + m into four int32 accumulators. Against x~ . y~, t leaves out the
+// products with n + m >= 6 and the remainders r: per d at most 3 * 64 * 64 * 2^-44 +
+// 2 * 64 * 64 * 2^-51 + 64 * 64 * 2^-58 + 2 * 2^-30 / 4 + 2^-60 < 1.5 * 2^-30, so
+// |t - x~ . y~| < 1.5 * 2^-23 over 128 d. In the head's frame (each key's t times 2^(F_j - Fmax),
 // Fmax the largest key exponent of the head: a power of two <= 1, so every row keeps its order)
-// the key floor(t 2^(F_j - Fmax + 27)) + 2^31, an integer shift of t 2^30, is off the exact
+// the key floor(t 2^(F_j - Fmax + 27)) + 2^31, an integer shift of t 2^37, is off the exact
 // canonical fp64 score in the same frame (whose own rounding is below 128 * 2^-53 * 8 = 2^-43) by
-// less than (2^-16 + 2^-24) / 2^-27 units: at most kBand / 2.
+// less than 1.5 * 2^-23 + 2^-26 (two key units) + 2^-43 < 1.75 * 2^-23: at most kBand / 2 units.
 //
 // Selection per row. A bitwise search with wave ballots, started below the bits all the row's keys
 // share and narrowed to one key per lane once at most 64 keys remain in play, puts the (k-1)-th
-// largest key K* in [T, T + 1023]; the (k-1)-th largest exact score then lies within kBand / 2 of
-// K*. Keys above T + 1023 + kBand are therefore strictly above it (kept), keys below T - kBand
+// largest key K* in [T, T + 15]; the (k-1)-th largest exact score then lies within kBand / 2 of
+// K*. Keys above T + 15 + kBand are therefore strictly above it (kept), keys below T - kBand
 // strictly below it (dropped), whatever the ties. The keys left in the band number at least the
 // picks still owed; when they number more, only their canonical fp64 scores are computed and the
 // owed picks go to the largest, ties to the lower j (-0.0 equal to +0.0).
@@ -432,6 +437,7 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
     constexpr int kPad = 128 * KG;                       // key columns held
     constexpr int kRows = 16 * kSelU * (kSelWaves / KG); // query rows per workgroup
     constexpr int kChunks = D / 64;
+    constexpr int kParts = D / 16;                       // 16-byte pieces of a limb vector
     constexpr int kM = kPad / kWave;                     // keys per lane in the selection
     constexpr int kTiles = 8;                            // 16-key tiles per wavefront
     __shared__ uint32_t keys[kRows * kPad];              // 64 KB per 16-row tile per wavefront
@@ -441,9 +447,14 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
     __shared__ int fmax_w[kSelWaves];
     if (gate != nullptr && *gate == 0.0) return;         // the mask of an earlier step is kept
 
+    // Hardware deals workgroup ids round-robin over the 8 XCDs: XCD x takes heads x, x + 8, ... one
+    // after another, all strips of a head together, so the head's key limbs (512 KB) are read from
+    // that XCD's L2 by every strip.
     const int strips = (nB + kRows - 1) / kRows;
-    const int64_t bh = blockIdx.x / strips;
-    const int i0 = (int)(blockIdx.x % strips) * kRows;
+    const int64_t seq = blockIdx.x / kNumXcd;           // position in the XCD's sequence
+    const int64_t bh = (seq / strips) * kNumXcd + blockIdx.x % kNumXcd;
+    if (bh >= BH) return;
+    const int i0 = (int)(seq % strips) * kRows;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
@@ -465,8 +476,8 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
             for (int a = 0; a < kLimbs; ++a)
 #pragma unroll
                 for (int c = 0; c < kChunks; ++c)
-                    qa[u][a][c] = *(const int32x4*)(ql + ((int64_t)a * kPad + i0 + 16 * (kSelU * p + u) + lr) * D +
-                                                    64 * c + 16 * lg);
+                    qa[u][a][c] = *(const int32x4*)(ql + ((int64_t)(a * kParts + 4 * c + lg) * kPad + i0 +
+                                                          16 * (kSelU * p + u) + lr) * 16);
         // a tile's key limbs and exponent are loaded together, one tile ahead of their use
         auto load_k = [&](int t, int32x4 (&kb)[kLimbs][kChunks], int& f) {
             const int j = 128 * kg + 16 * t + lr;
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
             for (int a = 0; a < kLimbs; ++a)
 #pragma unroll
                 for (int c = 0; c < kChunks; ++c)
-                    kb[a][c] = *(const int32x4*)(kl + ((int64_t)a * kPad + j) * D + 64 * c + 16 * lg);
+                    kb[a][c] = *(const int32x4*)(kl + ((int64_t)(a * kParts + 4 * c + lg) * kPad + j) * 16);
             f = ke[j];
         };
         int32x4 kb0[kLimbs][kChunks], kb1[kLimbs][kChunks];
@@ -494,32 +505,31 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
         for (int w = 1; w < kSelWaves; ++w) fmax = max(fmax, fmax_w[w]);
 
         auto tile = [&](int t, const int32x4 (&kb)[kLimbs][kChunks], int fj) {
-            int32x4 g[kSelU][3];
+            int32x4 g[kSelU][kLimbs];                    // g[.][n]: limb pairs with index sum n (0-based)
 #pragma unroll
             for (int u = 0; u < kSelU; ++u)
 #pragma unroll
-                for (int n = 0; n < 3; ++n) g[u][n] = int32x4{0, 0, 0, 0};
+                for (int n = 0; n < kLimbs; ++n) g[u][n] = int32x4{0, 0, 0, 0};
 #pragma unroll
             for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-                for (int u = 0; u < kSelU; ++u) {
-                    g[u][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[0][c], g[u][0], 0, 0, 0);
-                    g[u][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[1][c], g[u][1], 0, 0, 0);
-                    g[u][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][1][c], kb[0][c], g[u][1], 0, 0, 0);
-                    g[u][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][0][c], kb[2][c], g[u][2], 0, 0, 0);
-                    g[u][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][1][c], kb[1][c], g[u][2], 0, 0, 0);
-                    g[u][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][2][c], kb[0][c], g[u][2], 0, 0, 0);
-                }
+                for (int u = 0; u < kSelU; ++u)
+#pragma unroll
+                    for (int n = 0; n < kLimbs; ++n)
+#pragma unroll
+                        for (int a = 0; a <= n; ++a)
+                            g[u][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[u][a][c], kb[n - a][c], g[u][n], 0, 0, 0);
             // output element r of lane l: row 4 * (l / 16) + r of the tile, key column l % 16
             const int j = 128 * kg + 16 * t + lr;
-            const int shift = min(fmax - fj + 3, 63);     // >= 3
+            const int shift = min(fmax - fj + 10, 63);    // t 2^37 -> t 2^(27 + F_j - Fmax); >= 10
 #pragma unroll
             for (int u = 0; u < kSelU; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t t30 = ((int64_t)g[u][0][r] << 14) + ((int64_t)g[u][1][r] << 7) + (int64_t)g[u][2][r];
+                    const int64_t t37 = ((int64_t)g[u][0][r] << 21) + ((int64_t)g[u][1][r] << 14) +
+                                        ((int64_t)g[u][2][r] << 7) + (int64_t)g[u][3][r];
                     const int row = 16 * (kSelU * p + u) + 4 * lg + r;
-                    keys[row * kPad + j] = (uint32_t)(int32_t)(t30 >> shift) ^ 0x80000000u;
+                    keys[row * kPad + j] = (uint32_t)(int32_t)(t37 >> shift) ^ 0x80000000u;
                 }
         };
 #pragma unroll 1
@@ -725,7 +735,8 @@ void launch_filtered_kg(const double* pq, const double* pk, const int8_t* limbs,
                         hipStream_t stream) {
     constexpr int kRows = 16 * kSelU * (kSelWaves / KG);
     const int64_t strips = (nB + kRows - 1) / kRows;
-    hipLaunchKernelGGL((select_filtered_kernel<D, KG>), dim3((unsigned)(BH * strips)), dim3(kSelThreads), 0, stream,
+    const int64_t groups = (BH + kNumXcd - 1) / kNumXcd * kNumXcd * strips;
+    hipLaunchKernelGGL((select_filtered_kernel<D, KG>), dim3((unsigned)groups), dim3(kSelThreads), 0, stream,
                        pq, pk, limbs, kexp, mask, nB, kept, BH, gate);
 }
 
@@ -752,10 +763,11 @@ hipError_t launch_filtered(const double* pq, void* tail, uint8_t* mask, int32_t 
 
 size_t select_workspace_bytes(int64_t B, int64_t H, int64_t nB, int64_t D) {
     const size_t pooled = ((size_t)2 * B * H * nB * D * sizeof(double) + 255) / 256 * 256;
-    // nB <= 1024: int8 limbs [2][B,H][3][nBpad][D] + k exponents [B,H][nBpad] (6D + 4 <= 8D bytes per
-    // padded block and head); beyond: the uint64 score keys [B,H,nB,nB]
-    const size_t tail = nB <= kFusedMaxBlocks ? (size_t)B * H * D * fused_pad((int)nB) * sizeof(double)
-                                              : (size_t)B * H * nB * nB * sizeof(uint64_t);
+    // nB <= 1024: int8 limbs [2][B,H][4][nBpad][D] + k exponents [B,H][nBpad] int32; beyond: the
+    // uint64 score keys [B,H,nB,nB]
+    const size_t tail = nB <= kFusedMaxBlocks
+                            ? (size_t)B * H * fused_pad((int)nB) * ((size_t)2 * kLimbs * D + sizeof(int32_t))
+                            : (size_t)B * H * nB * nB * sizeof(uint64_t);
     return pooled + tail;
 }
 

@@ -59,14 +59,14 @@ def test_kept_blocks_errors():
 
 def test_workspace_bytes():
     lib = _binding.lib()
-    # pooled means of q and k (padded to 256 bytes), then for nB <= 1024 the k means transposed with nB
-    # padded to 256/512/1024, beyond that the uint64 score keys
+    # pooled means of q and k (padded to 256 bytes), then for nB <= 1024 four int8 limbs of every q and k
+    # mean and an int32 exponent per k mean, nB padded to 256/512/1024; beyond that the uint64 score keys
     nB = 993
     pooled = (2 * 40 * nB * 128 * 8 + 255) // 256 * 256
-    assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 128, 128) == pooled + 40 * 128 * 1024 * 8
+    assert lib.saq_select_blocks_workspace_bytes(1, 127040, 40, 128, 128) == pooled + 40 * 1024 * (2 * 4 * 128 + 4)
     nB = 200
     pooled = (2 * 3 * nB * 64 * 8 + 255) // 256 * 256
-    assert lib.saq_select_blocks_workspace_bytes(1, 200 * 64, 3, 64, 64) == pooled + 3 * 64 * 256 * 8
+    assert lib.saq_select_blocks_workspace_bytes(1, 200 * 64, 3, 64, 64) == pooled + 3 * 256 * (2 * 4 * 64 + 4)
     nB = 2000
     pooled = (2 * 2 * nB * 128 * 8 + 255) // 256 * 256
     assert lib.saq_select_blocks_workspace_bytes(1, 2000 * 128, 2, 128, 128) == pooled + 2 * nB * nB * 8
