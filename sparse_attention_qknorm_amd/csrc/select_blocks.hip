@@ -387,10 +387,12 @@ __device__ __forceinline__ double canonical_score_lds(const double* x, const dou
     return s;
 }
 
-// The same score with the key mean in memory, as a plain call, for the rare wide bands.
+// The same score with the key mean (block j of pk) in memory, as a plain call, for the rare wide
+// bands; the address is formed here so that no per-slot pointer stays live in the caller.
 template <int D>
-__device__ __noinline__ double canonical_score_call(const double* x, const double* __restrict__ y) {
+__device__ __noinline__ double canonical_score_call(const double* x, const double* __restrict__ pk, int j) {
 #pragma clang fp contract(off)
+    const double* y = pk + (int64_t)j * D;
     double s = 0.0;
     for (int d = 0; d < D; ++d) {
         const double prod = x[d] * y[d];
@@ -476,16 +478,18 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
             for (int a = 0; a < kLimbs; ++a)
 #pragma unroll
                 for (int c = 0; c < kChunks; ++c)
-                    qa[u][a][c] = *(const int32x4*)(ql + ((int64_t)(a * kParts + 4 * c + lg) * kPad + i0 +
-                                                          16 * (kSelU * p + u) + lr) * 16);
+                    qa[u][a][c] = *(const int32x4*)(ql + (size_t)(a * kParts + 4 * c) * kPad * 16 +
+                                                    (uint32_t)((lg * kPad + i0 + 16 * (kSelU * p + u) + lr) * 16));
         // a tile's key limbs and exponent are loaded together, one tile ahead of their use
+        // (uniform bases per limb piece plus one 32-bit lane offset, so the loads take scalar bases)
         auto load_k = [&](int t, int32x4 (&kb)[kLimbs][kChunks], int& f) {
             const int j = 128 * kg + 16 * t + lr;
+            const uint32_t off = (uint32_t)((lg * kPad + j) * 16);
 #pragma unroll
             for (int a = 0; a < kLimbs; ++a)
 #pragma unroll
                 for (int c = 0; c < kChunks; ++c)
-                    kb[a][c] = *(const int32x4*)(kl + ((int64_t)(a * kParts + 4 * c + lg) * kPad + j) * 16);
+                    kb[a][c] = *(const int32x4*)(kl + (size_t)(a * kParts + 4 * c) * kPad * 16 + off);
             f = ke[j];
         };
         int32x4 kb0[kLimbs][kChunks], kb1[kLimbs][kChunks];
@@ -693,7 +697,7 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
 #pragma unroll
                     for (int m = 0; m < kM; ++m)
                         ek[m] = ((band >> m) & 1u)
-                                    ? order_key(canonical_score_call<D>(xrow[wave], pkh + (int64_t)(lane + kWave * m) * D))
+                                    ? order_key(canonical_score_call<D>(xrow[wave], pkh, lane + kWave * m))
                                     : 0ull;
                     uint64_t T64 = 0;
                     for (int b64 = 63; b64 >= 0; --b64) {
