@@ -302,14 +302,16 @@ constexpr int kSearchLowBit = 4;          // the threshold search resolves key b
 constexpr uint32_t kBand = 56;
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kSelU = 1;                  // 16-row query tiles per wavefront in the score phase
+// 16-row query tiles per wavefront in the score phase. Two would halve the key-limb reads but
+// need 128 KB of keys per workgroup, one workgroup per CU: measured slower (0.26 vs 0.20 ms).
+constexpr int kSelU = 1;
 
 // pooled [2][BH][nB][D] fp64 -> limbs [2][BH][4][D/16][nBpad][16] int8 (16-byte pieces of the
 // vectors, piece-major so that 16 consecutive blocks' pieces are 256 contiguous bytes, the shape
-// of one MFMA operand load; zeros for j >= nB) and, for the k means, exponents [BH][nBpad]. A vector x with max |x_d| = f 2^F (f in [1/2, 1)) is scaled to
-// x~ = x 2^-(F+2), so |x~_d| < 1/4, and written as x~ = a1 2^-8 + a2 2^-15 + a3 2^-22 + a4 2^-29 + r:
-// each a_n rounds what is left to the nearest integer (|a_n| <= 64) and |r| <= 2^-30. Every step is
-// exact in fp64.
+// of one MFMA operand load; zeros for j >= nB) and, for the k means, exponents [BH][nBpad].
+// A vector x with max |x_d| = f 2^F (f in [1/2, 1)) is scaled to x~ = x 2^-(F+2), so |x~_d| < 1/4,
+// and written as x~ = a1 2^-8 + a2 2^-15 + a3 2^-22 + a4 2^-29 + r: each a_n rounds what is left
+// to the nearest integer (|a_n| <= 64) and |r| <= 2^-30. Every step is exact in fp64.
 template <int D>
 __global__ __launch_bounds__(kThreads) void limbs_kernel(const double* __restrict__ pooled, int8_t* __restrict__ limbs,
                                                          int32_t* __restrict__ kexp, int64_t BH, int32_t nB,
@@ -411,7 +413,7 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// One workgroup of 8 wavefronts per (b, h, strip of 32 * 8/KG query rows); nBpad = 128 * KG.
+// One workgroup of 8 wavefronts per (b, h, strip of 16 * 8/KG query rows); nBpad = 128 * KG.
 //
 // Approximate scores. With the limbs above, P_nm = sum_d a_n[d] b_m[d] is an exact integer
 // (v_mfma_i32_16x16x64_i8), and so is t 2^37 = sum over n + m <= 5 of P_nm 2^(7 (5 - n - m)):
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
     constexpr int kParts = D / 16;                       // 16-byte pieces of a limb vector
     constexpr int kM = kPad / kWave;                     // keys per lane in the selection
     constexpr int kTiles = 8;                            // 16-key tiles per wavefront
-    __shared__ uint32_t keys[kRows * kPad];              // 64 KB per 16-row tile per wavefront
+    __shared__ uint32_t keys[kRows * kPad];              // 64 KB: two workgroups per CU
     __shared__ __attribute__((aligned(16))) double xrow[kSelWaves][D];
     __shared__ uint32_t slot[kSelWaves][kWave];
     __shared__ int pick_s[kSelWaves][kWave];
@@ -462,7 +464,7 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
     const int lane = tid % kWave;
     const int32_t* ke = kexp + bh * kPad;
 
-    // ---- approximate keys: wavefront = 32 query rows (two 16-row tiles) x 128 key blocks
+    // ---- approximate keys: wavefront = kSelU 16-row query tiles x 128 key blocks
     {
         const int p = wave / KG;
         const int kg = wave % KG;
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
     for (int r = wave; r < kRows; r += kSelWaves) {
         const int i = i0 + r;
         if (i >= nB) break;
-        // valid keys lie in (2^30, 3 * 2^30); 0 marks j >= nB and the diagonal
+        // valid keys lie within 2^30 + 1 of 2^31 (|t| < 8); 0 marks j >= nB and the diagonal
         uint32_t key[kM];
 #pragma unroll
         for (int m = 0; m < kM; ++m) {

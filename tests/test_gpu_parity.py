@@ -177,6 +177,28 @@ def test_near_tie_scores(S, H, D, block, keep, scale_period):
     log(f"  near-tie scores S={S} D={D} block={block} keep={keep} scales={scale_period}: masks equal the oracle's")
 
 
+@pytest.mark.parametrize("D,keep", [(64, 0.5), (128, 0.35), (128, 0.6)])
+def test_mixed_scale_selection(D, keep):
+    # Key blocks at very different scales: every fifth block scaled by 2^-28 (its scores sit within
+    # about 2^-28 of zero next to ordinary ones), every seventh all zero, the rest at 2^-1..2^1.
+    # Rows whose threshold falls among the near-zero scores must be split by exact fp64 scores.
+    S, H, block = 300 * 64 - 17, 2, 64
+    rng = np.random.Generator(np.random.PCG64(31 + D))
+    kf = rng.standard_normal((1, S, H, D)).astype(np.float32)
+    kf = np.sign(kf) * np.maximum(np.abs(kf), 2.0 ** -7)      # keeps every non-zero |x| >= 2^-35
+    for j in range(-(-S // block)):
+        sl = slice(j * block, (j + 1) * block)
+        kf[0, sl] *= 0.0 if j % 7 == 0 else 2.0 ** -28 if j % 5 == 0 else 2.0 ** (j % 3 - 1)
+    k = torch.from_numpy(kf).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((1, S, H, D)).astype(np.float32)).to(torch.bfloat16)
+    assert pooled_exactness_ok(to64(k)) and pooled_exactness_ok(to64(q))
+    mask = saq.select_blocks(q.to(DEV), k.to(DEV), keep, block).cpu().numpy()
+    ref = oracle_mask(to64(q), to64(k), block, keep)
+    for (b, h), m in ref.items():
+        assert np.array_equal(mask[b, h], m), f"mask differs on head {h}"
+    log(f"  mixed-scale key blocks D={D} keep={keep}: masks equal the oracle's")
+
+
 def test_user_mask_with_empty_rows_and_all_ones():
     inp = synth.make_small_case(700, 2, 128, seed=3, sections=(32, 48, 48), T=1, Hg=20, W=30)
     g = _upload(inp)
