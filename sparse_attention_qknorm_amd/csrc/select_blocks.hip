@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kSelThreads, kSelU == 1 ? 4 : 2) void select_filter
     constexpr int kParts = D / 16;                       // 16-byte pieces of a limb vector
     constexpr int kM = kPad / kWave;                     // keys per lane in the selection
     constexpr int kTiles = 8;                            // 16-key tiles per wavefront
-    __shared__ uint32_t keys[kRows * kPad];              // 64 KB: two workgroups per CU
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kRows * kPad];   // 64 KB: two workgroups per CU
     __shared__ __attribute__((aligned(16))) double xrow[kSelWaves][D];
     __shared__ uint32_t slot[kSelWaves][kWave];
     __shared__ int pick_s[kSelWaves][kWave];
