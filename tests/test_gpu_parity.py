@@ -199,6 +199,39 @@ def test_mixed_scale_selection(D, keep):
     log(f"  mixed-scale key blocks D={D} keep={keep}: masks equal the oracle's")
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_selection_random_cases(case):
+    # Seeded random shapes across the selection kernel's three strip layouts (nB padded to 256, 512,
+    # 1024), both head sizes and block sizes, keep ratios from 0.03 to 0.97, per-block scales from
+    # 2^-20 to 2, some all-zero blocks and some repeated blocks; masks must equal the oracle's.
+    rng = np.random.Generator(np.random.PCG64(500 + case))
+    D = (64, 128)[case % 2]
+    block = (64, 128)[(case // 2) % 2]
+    nB = int(rng.integers(2, 1025)) if case < 10 else (1024, 1000)[case - 10]
+    S = nB * block - int(rng.integers(0, block))
+    H = 1 if nB > 600 else 2
+    keep = float(rng.uniform(0.03, 0.97))
+    x = rng.standard_normal((2, 1, S, H, D)).astype(np.float32)
+    x = np.sign(x) * np.clip(np.abs(x), 2.0 ** -14, 7.0)
+    scale = 2.0 ** rng.integers(-20, 2, size=(2, nB))
+    scale[:, rng.random(nB) < 0.05] = 0.0
+    for t in range(2):
+        for j in range(nB):
+            x[t, 0, j * block:(j + 1) * block] *= scale[t, j]
+    rep = rng.random(nB) < 0.05                                  # repeat block 0 of k
+    for j in np.nonzero(rep)[0]:
+        n = min(block, S - j * block)
+        x[1, 0, j * block:j * block + n] = x[1, 0, :n]
+    q = torch.from_numpy(x[0]).to(torch.bfloat16)
+    k = torch.from_numpy(x[1]).to(torch.bfloat16)
+    assert pooled_exactness_ok(to64(q)) and pooled_exactness_ok(to64(k))
+    mask = saq.select_blocks(q.to(DEV), k.to(DEV), keep, block).cpu().numpy()
+    ref = oracle_mask(to64(q), to64(k), block, keep)
+    for (b, h), m in ref.items():
+        assert np.array_equal(mask[b, h], m), f"case {case}: mask differs on head {h} (nB={nB} D={D} keep={keep:.3f})"
+    log(f"  random selection case {case}: nB={nB} D={D} block={block} keep={keep:.3f}: masks equal the oracle's")
+
+
 def test_user_mask_with_empty_rows_and_all_ones():
     inp = synth.make_small_case(700, 2, 128, seed=3, sections=(32, 48, 48), T=1, Hg=20, W=30)
     g = _upload(inp)
