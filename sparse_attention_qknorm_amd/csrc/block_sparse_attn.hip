@@ -272,6 +272,11 @@ __global__ __launch_bounds__(BLOCK * 2) void block_sparse_attn_kernel(
 // next d-step's K fragments, the next key step's V^T fragments), with the order
 // pinned by scheduling-group barriers; the transposed-V read addresses are
 // precomputed per lane (eight base offsets, the key step only adds 16 rows).
+// Three workgroup barriers per tile: K_n landed; after QK^T, V_n landed and K_n
+// released (the K_{n+1} copy is issued there, and softmax runs straight into
+// PV without a barrier between them); after PV, V_n released (V_{n+1} issued).
+// Folding the V wait into the post-QK^T barrier instead of a fourth barrier
+// before PV was measured 4% faster with the same output bits.
 namespace d128 {
 
 constexpr int kBlock = 128;
@@ -300,8 +305,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // The tile loop. The two LDS tiles come in as separate __restrict__ pointers:
 // once inlined, the compiler's wait-count pass can then tell the K and V
-// direct-to-LDS copies apart, so reading V waits only for V's copy and not for
-// the K prefetch of the next tile issued just before.
+// direct-to-LDS copies apart, so reading V does not wait for the K prefetch of
+// the next tile.
 __device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* __restrict__ v_lds,
                                           const uint16_t* __restrict__ kept, int n_kept,
                                           const __amdgpu_buffer_rsrc_t& rk, const __amdgpu_buffer_rsrc_t& rv,
@@ -393,7 +398,8 @@ __device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* 
             if (st + 1 < kD / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
-        __syncthreads();                               // every wave is done with K_n
+        wait_vmcnt<0>();                               // V_n landed
+        __syncthreads();                               // ... and every wave is done with K_n
         if (more) issue_k(kept[n + 1]);
 
         // ---- softmax
@@ -435,9 +441,6 @@ __device__ __forceinline__ void tile_loop(uint8_t* __restrict__ k_lds, uint8_t* 
         }
 
         // ---- O^T += V^T P^T
-        if (more) wait_vmcnt<kLoadsPerWave>();         // V_n landed; K_{n+1} may be in flight
-        else wait_vmcnt<0>();
-        __syncthreads();
         // the next key step's four V^T fragments are read while this step's four MFMAs run
         bf16x4 va[2][kD / 32][2];
 #pragma unroll
