@@ -18,9 +18,11 @@
 // workgroup per tile, heads fastest in the launch order so that neighbouring
 // workgroups stream neighbouring bytes of the same token rows; each thread keeps
 // its chunks of the tile in registers between the amax pass and the encode pass,
-// so the input is read once.
+// so the input is read once. Inputs and outputs move with nontemporal accesses
+// (stream_io.h).
 #include "common.h"
 #include "kernels.h"
+#include "stream_io.h"
 
 namespace saq {
 
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restr
         const int r = c / T::kChunksPerRow;
         const int cc = c % T::kChunksPerRow;
         if (r < t.n) {
-            v[j] = x[(row0 + (int64_t)r * H) * T::kChunksPerRow + cc];
+            v[j] = load_once(&x[(row0 + (int64_t)r * H) * T::kChunksPerRow + cc]);
             amax = abs_max_bits(amax, v[j].x);
             amax = abs_max_bits(amax, v[j].y);
             amax = abs_max_bits(amax, v[j].z);
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restr
             out.x = encode_int8x4(p[0], p[1], p[2], p[3]);
             out.y = encode_int8x4(p[4], p[5], p[6], p[7]);
         }
-        codes[(row0 + (int64_t)r * H) * T::kChunksPerRow + cc] = out;
+        store_once(&codes[(row0 + (int64_t)r * H) * T::kChunksPerRow + cc], out);
     }
 }
 
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint2* __res
         const int cc = c % T::kChunksPerRow;
         if (r >= t.n) continue;
         const int64_t idx = (row0 + (int64_t)r * H) * T::kChunksPerRow + cc;
-        const uint2 q = codes[idx];
+        const uint2 q = load_once(&codes[idx]);
         const uint32_t w[2] = {q.x, q.y};
         uint32_t o[4];
 #pragma unroll
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint2* __res
             o[2 * e] = f32_to_bf16_bits(f[0] * s) | (f32_to_bf16_bits(f[1] * s) << 16);
             o[2 * e + 1] = f32_to_bf16_bits(f[2] * s) | (f32_to_bf16_bits(f[3] * s) << 16);
         }
-        y[idx] = make_uint4(o[0], o[1], o[2], o[3]);
+        store_once(&y[idx], make_uint4(o[0], o[1], o[2], o[3]));
     }
 }
 

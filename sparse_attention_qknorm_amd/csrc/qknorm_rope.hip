@@ -16,6 +16,7 @@
 // (token, head) for the read and write of q and k.
 #include "common.h"
 #include "kernels.h"
+#include "stream_io.h"
 
 namespace saq {
 
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(
         for (int j = 0; j < kBatch; ++j) {
             const int c = c0 + j * kThreads;
             if (c < total) {
-                raw[j] = c < chunks_per_tensor ? q_in[base + c] : k_in[base + c - chunks_per_tensor];
+                raw[j] = c < chunks_per_tensor ? load_once(&q_in[base + c]) : load_once(&k_in[base + c - chunks_per_tensor]);
             }
         }
 #pragma unroll
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(kThreads) void qknorm_rope_kernel(
                 for (int e = 0; e < 8; ++e) w[e] = is_q ? wq[e] : wk[e];
                 double unused[8];
                 const uint4 o = norm_rope_chunk<false, kLanesPerRow>(raw[j], w, rot, eps, 1.0f / D, unused);
-                if (is_q) q_out[base + c] = o;
-                else k_out[base + c - chunks_per_tensor] = o;
+                if (is_q) store_once(&q_out[base + c], o);
+                else store_once(&k_out[base + c - chunks_per_tensor], o);
             }
         }
     }
@@ -238,8 +239,8 @@ __global__ __launch_bounds__(kMaxThreads) void qknorm_rope_pool_kernel(
 #pragma unroll
         for (int a = 0; a < kDepth; ++a)
             if (a < n) {
-                rq[a] = q_in[row0 + (int64_t)a * P];
-                rk[a] = k_in[row0 + (int64_t)a * P];
+                rq[a] = load_once(&q_in[row0 + (int64_t)a * P]);
+                rk[a] = load_once(&k_in[row0 + (int64_t)a * P]);
             }
     }
     const uint4* qsrc = q_in + row0 + (int64_t)kDepth * P;     // token t + kDepth
@@ -261,16 +262,16 @@ __global__ __launch_bounds__(kMaxThreads) void qknorm_rope_pool_kernel(
                 rk[a] = rk[a + 1];
             }
             if (t + kDepth < n) {
-                rq[kDepth - 1] = *qsrc;
-                rk[kDepth - 1] = *ksrc;
+                rq[kDepth - 1] = load_once(qsrc);
+                rk[kDepth - 1] = load_once(ksrc);
             }
             qsrc += P;
             ksrc += P;
             float2 rot[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) rot[p] = cs[(t / kTokChunk) & 1][tt][lane_in_row * 4 + p];
-            *qdst = norm_rope_chunk<true, kLanesPerRow>(cq, wq, rot, eps, 1.0f / D, accq);
-            *kdst = norm_rope_chunk<true, kLanesPerRow>(ck, wk, rot, eps, 1.0f / D, acck);
+            store_once(qdst, norm_rope_chunk<true, kLanesPerRow>(cq, wq, rot, eps, 1.0f / D, accq));
+            store_once(kdst, norm_rope_chunk<true, kLanesPerRow>(ck, wk, rot, eps, 1.0f / D, acck));
             qdst += P;
             kdst += P;
         }

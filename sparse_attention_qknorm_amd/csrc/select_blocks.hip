@@ -41,6 +41,7 @@
 // produces the same scores bit for bit.
 #include "common.h"
 #include "kernels.h"
+#include "stream_io.h"
 
 namespace saq {
 
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const uint4* __restrict_
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     for (int t = t0 + row0; t < t1; t += kRowsPerPass) {
-        const uint4 raw = x[((b * S + t) * H + h) * kLanesPerRow + lane];
+        const uint4 raw = load_once(&x[((b * S + t) * H + h) * kLanesPerRow + lane]);
         const uint32_t w32[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
