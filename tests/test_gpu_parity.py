@@ -251,6 +251,34 @@ def test_user_mask_with_empty_rows_and_all_ones():
                     "all-ones mask vs dense")
 
 
+@pytest.mark.parametrize("order", ["ascending", "descending", "mixed"])
+def test_large_score_jumps_between_tiles(order):
+    # Key blocks at magnitudes 2^-6 .. 2^5, in ascending, descending or shuffled order along the key axis, so a
+    # row's running maximum moves by tens of log2 units from one kept tile to the next (far beyond the lazy
+    # rescale threshold) or stays far above every later tile. Head 0 attends densely, head 1 through a random
+    # mask with the diagonal; the last block is partial. The online softmax must give the plain softmax.
+    S, H, D, block = 12 * 128 + 40, 2, 128, 128
+    nB = (S + block - 1) // block
+    rng = np.random.Generator(np.random.PCG64({"ascending": 11, "descending": 12, "mixed": 13}[order]))
+    f = 2.0 ** np.linspace(-6, 5, nB)
+    if order == "descending":
+        f = f[::-1]
+    elif order == "mixed":
+        f = rng.permutation(f)
+    q = rng.standard_normal((1, S, H, D))
+    k = rng.standard_normal((1, S, H, D))
+    for j in range(nB):
+        k[:, j * block:(j + 1) * block] *= f[j]
+    v = rng.uniform(-1.0, 1.0, (1, S, H, D))
+    qt, kt, vt = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16) for x in (q, k, v))
+    m = np.ones((1, H, nB, nB), dtype=np.uint8)
+    m[0, 1] = rng.random((nB, nB)) < 0.5
+    m[0, 1][np.arange(nB), np.arange(nB)] = 1
+    o = saq.block_sparse_attn(qt.to(DEV), kt.to(DEV), vt.to(DEV), torch.from_numpy(m).to(DEV), block)
+    ref = oracle.block_sparse_attention(to64(qt), to64(kt), to64(vt), m, block)
+    check_attention(to64(o), ref, f"score jumps between tiles ({order})")
+
+
 def test_constant_v_gives_constant_output():
     inp = synth.make_small_case(300, 1, 64, seed=5, sections=(16, 24, 24))
     g = _upload(inp)
