@@ -68,7 +68,9 @@ enum saq_status {
  * The norm and rotation run in fp32 (angles in fp64), the result is rounded
  * to bf16 (nearest-even) and written back in place.
  *
- *   q, k     bf16 [B,S,H,D], read and overwritten.
+ *   q, k     bf16 [B,S,H,D], read and overwritten. Any finite values: a row
+ *            whose fp32 sum of squares would overflow (entries beyond about
+ *            2^60) is normalised through a pass scaled by 2^-68.
  *   pos_thw  int32 [S,3] device array of (t, h, w) positions, shared by all
  *            batch entries; any values are allowed.
  *   w_q, w_k fp32 [D] device arrays.

@@ -62,7 +62,21 @@ __device__ __forceinline__ uint4 norm_rope_chunk(const uint4 raw, const float (&
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
     ss = row_sum<kLanesPerRow>(ss);
-    const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, inv_d, eps));
+    float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, inv_d, eps));
+    if (__builtin_isinf(ss)) {
+        // A row with entries beyond about 2^60 overflows the fp32 sum of squares. Every lane of the row
+        // takes this branch (they hold the same sum). Redo the sum on x * 2^-68, exact and finite for
+        // every finite bf16 x, and scale back: rsqrt(sum(x^2)/D) = rsqrt(sum((x 2^-68)^2)/D) * 2^-68.
+        // eps * 2^-136 would be lost against any such mean square, so it is left out.
+        float ss2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xs = x[e] * 0x1p-68f;
+            ss2 = __builtin_fmaf(xs, xs, ss2);
+        }
+        ss2 = row_sum<kLanesPerRow>(ss2);
+        rinv = __builtin_amdgcn_rsqf(ss2 * inv_d) * 0x1p-68f;
+    }
     uint32_t outw[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {

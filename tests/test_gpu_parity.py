@@ -279,6 +279,36 @@ def test_large_score_jumps_between_tiles(order):
     check_attention(to64(o), ref, f"score jumps between tiles ({order})")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prologue_rows_beyond_fp32_square_range(D):
+    # Rows whose entries reach 2^61 .. 2^126, and one row of the largest finite bf16 throughout: their fp32
+    # sum of squares overflows, so the norm takes its rescaled pass. Ordinary rows of the same tokens and
+    # heads sit beside them. Both prologue kernels (in place, and fused with the pooling) against the oracle.
+    sections = (D // 4, 3 * D // 8, 3 * D // 8)
+    inp = synth.make_small_case(300, 2, D, seed=9 + D, sections=sections, T=2, Hg=6, W=10)
+    q, k = inp["q"].double().clone(), inp["k"].double().clone()
+    for n, e in enumerate((61, 75, 100, 126)):
+        for x, t, h in ((q, 10 + n, 0), (k, 130 + n, 1)):
+            x[0, t, h] = x[0, t, h] / x[0, t, h].abs().max() * 2.0 ** e
+    q[0, 40, 1] = float(torch.finfo(torch.bfloat16).max)
+    k[0, 299, 0] = -float(torch.finfo(torch.bfloat16).max)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    assert torch.isfinite(q.float()).all() and torch.isfinite(k.float()).all()
+    rq, rk = oracle.qknorm_rope(to64(q), to64(k), inp["pos_thw"].numpy(), inp["w_q"].numpy(), inp["w_k"].numpy(),
+                                sections, 10000.0, 1e-6)
+    g = _upload(inp)
+    qh, kh = q.to(DEV), k.to(DEV)
+    saq.qknorm_rope(qh, kh, g["pos_thw"], (g["w_q"], g["w_k"]), sections)
+    check_prologue(to64(qh), rq, f"D={D} huge rows q_hat")
+    check_prologue(to64(kh), rk, f"D={D} huge rows k_hat")
+    qf, kf = torch.empty_like(qh), torch.empty_like(kh)
+    saq.qknorm_rope_pool(q.to(DEV), k.to(DEV), qf, kf, g["pos_thw"], (g["w_q"], g["w_k"]), sections, block=64)
+    torch.cuda.synchronize()
+    assert torch.equal(qf, qh) and torch.equal(kf, kh)
+    assert abs(to64(qh)[0, 40, 1]).max() < 2 * np.sqrt(D)      # normalised, not zero
+    assert abs(to64(qh)[0, 40, 1]).max() > 0.1
+
+
 def test_constant_v_gives_constant_output():
     inp = synth.make_small_case(300, 1, 64, seed=5, sections=(16, 24, 24))
     g = _upload(inp)
