@@ -169,6 +169,11 @@ int saq_select_blocks_noalloc(const void* q, const void* k, int32_t B, int32_t S
  *
  *   softmax_scale  > 0, or <= 0 to mean 1/sqrt(D); must be finite.
  *   o              bf16 [B,S,H,D]; must not overlap q, k, v or block_mask.
+ *   q, k, v        finite, and small enough that the fp32 accumulations stay
+ *                  finite: the scores q.k * scale, and sums of up to S products
+ *                  of v with weights <= 2^8. |q|, |k| <= 2^55 and |v| <= 2^90
+ *                  suffice (D <= 128, S <= 2^20); beyond that o is undefined.
+ *                  Outputs of saq_qknorm_rope are always in range.
  */
 int saq_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* block_mask,
                           int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
