@@ -173,7 +173,7 @@ int saq_select_blocks_noalloc(const void* q, const void* k, int32_t B, int32_t S
  *                  finite: the scores q.k * scale, and sums of up to S products
  *                  of v with weights <= 2^8. |q|, |k| <= 2^55 and |v| <= 2^90
  *                  suffice (D <= 128, S <= 2^20); beyond that o is undefined.
- *                  Outputs of saq_qknorm_rope are always in range.
+ *                  Outputs of saq_qknorm_rope with weights |w| <= 2^40 are.
  */
 int saq_block_sparse_attn(const void* q, const void* k, const void* v, const uint8_t* block_mask,
                           int32_t B, int32_t S, int32_t H, int32_t D, int32_t block,
