@@ -19,6 +19,7 @@ the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -73,6 +74,19 @@ def measured_traffic(kernel_hash: str, workload: str, keep: float, path: str):
             or path == "folded"):
         return None
     return rec.get("bytes_per_launch")
+
+
+def config_for(name: str, seed=None):
+    """The named workload's config, with its seed index replaced when `seed` is given: other draws of the
+    same shapes, value distributions and structure."""
+    from sparse_attention_qknorm_amd import synth
+    cfg = synth.get_config(name)
+    return cfg if seed is None else dataclasses.replace(cfg, index=int(seed))
+
+
+def default_seed(cfg) -> bool:
+    from sparse_attention_qknorm_amd import synth
+    return cfg.index == synth.get_config(cfg.name).index
 
 
 def cpu_baseline(inp, cfg, keep: float, budget_s: float) -> dict:
@@ -155,7 +169,7 @@ def sweep(args) -> dict:
     import sparse_attention_qknorm_amd as saq
     from sparse_attention_qknorm_amd import synth
 
-    cfg = synth.get_config("sweep")
+    cfg = config_for("sweep", args.seed)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     saq.lib()
@@ -276,7 +290,7 @@ def sweep(args) -> dict:
                                                for kp in keeps}} for r in rows]
     return {"workload": f"sweep: {cfg.steps} denoising steps of the full layer (S={cfg.S}, H={cfg.H}, D={cfg.D}), "
                         f"step s = bf16(X_base + {cfg.drift}*s*Delta)",
-            "keeps": keeps, "thresholds": thresholds, "per_step": per_step, "summary": summary}
+            "seed": cfg.index, "keeps": keeps, "thresholds": thresholds, "per_step": per_step, "summary": summary}
 
 
 def codec_bench(args) -> dict:
@@ -289,7 +303,7 @@ def codec_bench(args) -> dict:
     import sparse_attention_qknorm_amd as saq
     from sparse_attention_qknorm_amd import synth
 
-    cfg = synth.get_config("full")
+    cfg = config_for("full", args.seed)
     keep = args.keep if args.keep is not None else cfg.keep_ratios[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -362,7 +376,7 @@ def codec_bench(args) -> dict:
     return {"metric": "INT8 QKV / FP8 O block codecs: GB/s per kernel and error of the exchange formats",
             "n_gpus": 1, "data": "synthetic", "steps": args.steps, "warmup": args.warmup,
             "config": {"workload": f"full layer tensors [1, {S}, {H}, {D}], tile = {cfg.block} tokens x {D} "
-                                   f"channels of one head, keep_ratio={keep}"},
+                                   f"channels of one head, keep_ratio={keep}", "seed": cfg.index},
             "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "achieved": res["int8"]["quantize_gbs"], "frac": res["int8"]["quantize_frac_of_hbm_peak"],
                          "kernel": "quantize_kernel<128,128,int8>", "traffic": None},
@@ -386,6 +400,9 @@ def main(argv=None) -> int:
                          "split: the three separate calls qknorm_rope / select_blocks / block_sparse_attn; "
                          "folded: fused prologue, then attention with the selection inside the kernel "
                          "(block_sparse_attn_select)")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed index of the synthetic inputs (default: the workload's own); the committed traffic "
+                         "record is reported only for the default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention in the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -413,7 +430,7 @@ def main(argv=None) -> int:
     import sparse_attention_qknorm_amd as saq
     from sparse_attention_qknorm_amd import synth
 
-    cfg = synth.get_config(args.workload)
+    cfg = config_for(args.workload, args.seed)
     keep = args.keep if args.keep is not None else cfg.keep_ratios[0]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -491,7 +508,7 @@ def main(argv=None) -> int:
     att_s = ms["att"] / 1e3
     achieved = flops / att_s / 1e12
     khash = attn_source_hash()
-    traffic = measured_traffic(khash, cfg.name, keep, args.path)
+    traffic = measured_traffic(khash, cfg.name, keep, args.path) if default_seed(cfg) else None
     pro_bytes = 8.0 * cfg.D * cfg.H * cfg.B * cfg.S + 12.0 * cfg.S
 
     result = {
@@ -512,6 +529,7 @@ def main(argv=None) -> int:
                                f"D={cfg.D}, block={cfg.block}, keep_ratio={keep}",
                    "global_batch": cfg.B, "seq_len": cfg.S, "heads": cfg.H, "head_dim": cfg.D,
                    "block": cfg.block, "keep_ratio": keep, "kept_blocks_per_row": saq.kept_blocks(keep, nB),
+                   "seed": cfg.index,
                    "parallelism": "none (1 GPU)"},
         "ms_per_layer": ms_step,
         "path": args.path,

@@ -1,6 +1,6 @@
 """Host-side logic of bench.py (no GPU): the computed-FLOP count from a block
 mask, the rule for reporting the committed HBM traffic record, the source hash
-it is keyed on, and the refusal of more than one GPU."""
+it is keyed on, the --seed option, and the refusal of more than one GPU."""
 import json
 import os
 import sys
@@ -50,6 +50,19 @@ def test_committed_traffic_record_names_its_kernel():
     for key in ("kernel_hash", "config", "keep_ratio", "bytes_per_launch"):
         assert key in rec
     assert rec["bytes_per_launch"] > 0
+
+
+def test_seed_option_replaces_only_the_seed_index():
+    from sparse_attention_qknorm_amd import synth
+    base = synth.get_config("tiny")
+    assert bench.config_for("tiny") == base and bench.default_seed(base)
+    other = bench.config_for("tiny", base.index + 17)
+    assert other.index == base.index + 17 and not bench.default_seed(other)
+    assert (other.S, other.H, other.D, other.block, other.keep_ratios) == (base.S, base.H, base.D, base.block,
+                                                                            base.keep_ratios)
+    a, b = synth.make_inputs(base), synth.make_inputs(other)
+    assert a["q"].shape == b["q"].shape and not torch.equal(a["q"], b["q"])
+    assert torch.equal(a["pos_thw"], b["pos_thw"])                 # positions are structure, not draws
 
 
 def test_more_than_one_gpu_is_refused(capsys):
